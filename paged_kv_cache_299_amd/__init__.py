@@ -1,0 +1,11 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+The compute path is the C-ABI library libpa.so (hand-written HIP kernels);
+this package is the argument-marshalling layer above it plus host-side
+helpers (storage format, block manager, seeded workloads).
+"""
+from .layout import kv_cache_shapes, k_chunk, DTYPE_CODES  # noqa: F401
+from .binding import (  # noqa: F401
+    pa_write_kv, pa_decode, pa_copy_blocks, pa_status_str, library_path, load_library,
+    PAError,
+)
