@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path for one layer of one decode iteration: the new
+token of every sequence is written into its slot (pa_write_kv; for the
+copy-on-write workload the block copies come first, pa_copy_blocks), then
+pa_decode attends over every sequence's paged context.  Inputs are resident
+in HBM before timing starts.  Successive steps rotate over `--layers`
+independent KV pools (one per model layer, all sharing the block tables, as
+a real decode iteration does), so no step finds its K/V in the caches of the
+previous one.
+
+Prints ONE JSON line.  `value` = algorithmic bytes of the step / step time
+(GB/s, decimal), tokens/s = sequences / step time.  `roofline` covers
+pa_decode (its partition kernel plus the merge kernel, timed with HIP events
+on the launch stream).  `cpu_baseline` times the CPU oracle on the same
+inputs (layer 0) on this host's cores.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+
+WORKLOAD_TEXT = {
+    "llama3_8b": "Llama-3-8B-shaped GQA decode, one layer: 32 seqs, 32 q / 8 kv heads, D 128, "
+                 "B 16, ctx ~ U{128..4096}, pool 12,000 blocks, bf16",
+    "opt_13b": "OPT-13B-shaped MHA decode, one layer: 64 seqs, 40 heads, D 128, B 16, "
+               "ctx lognormal median 512 clipped [16, 2048], pool 10,000 blocks, fp16",
+    "parallel_sampling": "parallel sampling: 16 prompts x 8 samples, 32 heads, D 128, B 16, "
+                         "shared 1,024-token prompt + U{0..256} private tokens, bf16",
+    "parallel_sampling_cow": "parallel sampling with copy-on-write: 16 x 8 samples, 32 heads, "
+                             "1,016-token shared prompt, 112 block copies, bf16",
+    "long_ctx": "long-context split decode: 4 seqs, 32 q / 8 kv heads, D 128, B 16, ctx 32K / "
+                "64K / 96K / 128K, 512-token partitions, bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--layers", type=int, default=8, help="resident KV pools rotated per step")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition tokens for pa_decode (default: the workload's, else auto)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run torch's plain copy of a 1 GiB tensor (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counter scale)")
+    return ap.parse_args()
+
+
+def calibrate_copy(reps=5):
+    """Plain device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "reps": reps}),
+          flush=True)
+
+
+def raw_bits(t):
+    """numpy view of a CPU tensor's element bits (the oracle's input form)."""
+    import numpy as np
+    import torch
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def decode_bytes(ctx, S, Hq, Hkv, D, B, e):
+    """Algorithmic bytes of one decode: K+V of every valid token, q in, out,
+    the used block-table entries and the context lengths."""
+    kv = sum(2 * c * Hkv * D * e for c in ctx)
+    qo = 2 * S * Hq * D * e
+    table = 4 * sum(-(-c // B) for c in ctx) + 4 * S
+    return kv + qo + table
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
+              "single-device and this build measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_299_amd as pa
+    from paged_kv_cache_299_amd import workloads
+    from paged_kv_cache_299_amd.layout import ELEM_BYTES, kv_cache_shapes
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pa.load_library()  # fails loudly if libpa.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_setup = time.time()
+    case = workloads.CASES[args.workload](fill=False)
+    S, Hq, Hkv, D, B = case.num_seqs, case.num_heads, case.num_kv_heads, case.head_dim, \
+        case.block_size
+    NB, dt = case.num_blocks, case.dtype
+    e = ELEM_BYTES[dt]
+    part = args.partition if args.partition is not None else (case.partition_tokens or 0)
+    k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
+    gen = torch.Generator(device=dev)
+    pools = []
+    for layer in range(args.layers):
+        gen.manual_seed(1000 * case.seed + layer)
+        k = torch.randn(k_shape, generator=gen, device=dev, dtype=torch.float32).to(dt)
+        v = torch.randn(v_shape, generator=gen, device=dev, dtype=torch.float32).to(dt)
+        pools.append((k, v))
+    q = case.q.to(dev)
+    bt = case.block_tables.to(dev)
+    cl = case.context_lens.to(dev)
+    out = torch.empty_like(q)
+    steps = []
+    for st in case.steps:
+        if isinstance(st, workloads.CopyStep):
+            steps.append(("copy", st.block_mapping.to(dev)))
+        else:
+            steps.append(("write", st.k_new.to(dev), st.v_new.to(dev), st.slot_mapping.to(dev)))
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    ctx = case.context_lens.tolist()
+    dec_bytes = decode_bytes(ctx, S, Hq, Hkv, D, B, e)
+    step_bytes = dec_bytes
+    for st in case.steps:
+        if isinstance(st, workloads.CopyStep):
+            step_bytes += 2 * 2 * st.block_mapping.shape[0] * Hkv * B * D * e  # K+V, read+write
+        else:
+            T = st.slot_mapping.shape[0]
+            step_bytes += 2 * 2 * T * Hkv * D * e + 8 * T
+
+    def run_step(i, evs=None):
+        k, v = pools[i % len(pools)]
+        if evs is not None:
+            evs[0].record()
+        for st in steps:
+            if st[0] == "copy":
+                pa.pa_copy_blocks(k, v, st[1])
+            else:
+                pa.pa_write_kv(st[1], st[2], k, v, st[3])
+        if evs is not None:
+            evs[1].record()
+        pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part)
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    decode_ms = [a[1].elapsed_time(a[2]) for a in evs]
+    write_ms = [a[0].elapsed_time(a[1]) for a in evs]
+    dec_avg = statistics.fmean(decode_ms)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
+    cpu = None
+    if args.cpu_reps > 0:
+        import oracle
+        k0, v0 = pools[0]
+        run_step(0)
+        torch.cuda.synchronize()
+        kh, vh = raw_bits(k0.cpu()), raw_bits(v0.cpu())
+        code = pa.DTYPE_CODES[dt]
+        times = []
+        for _ in range(args.cpu_reps):
+            t = time.perf_counter()
+            oracle.decode(raw_bits(case.q), kh, vh, case.block_tables.numpy(),
+                          case.context_lens.numpy(), case.scale, num_kv_heads=Hkv, head_dim=D,
+                          block_size=B, k_x=16 // e, dtype=code)
+            times.append(time.perf_counter() - t)
+        t_med = statistics.median(times)
+        cpu = {"value": round(dec_bytes / t_med / 1e9, 3), "unit": "GB/s",
+               "tokens_per_s": round(S / t_med, 2), "seconds": round(t_med, 3),
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"the full workload (all {S} sequences, layer 0), pa_decode only, "
+                         f"median of {args.cpu_reps} runs, fp64"}
+        del kh, vh
+
+    rec = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s "
+                  "at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[dt],
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded block placement and context lengths)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+                   "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
+                   "partition_tokens": part or "auto", "layers_rotated": args.layers},
+        "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "step_bytes": int(step_bytes),
+        "decode_us": round(dec_avg * 1e3, 2),
+        "write_us": round(statistics.fmean(write_ms) * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "kernel": "pa_decode (partition + merge kernels)",
+                     "bytes_per_launch": int(dec_bytes)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * pa.h -- C ABI of libpa, paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the decode step of PagedAttention: every sequence keeps its
+ * keys and values in fixed-size physical blocks of B tokens that may sit
+ * anywhere in a pool, a per-sequence block table maps logical block i to a
+ * physical block, and the query of the newest token is scored against every
+ * cached token with a streaming (max / sum-of-exponentials) softmax.
+ *   [論文解説: PagedAttention — 仮想メモリ着想のKVキャッシュ管理でLLMサービングを高効率化,
+ *    技術的詳細 › PagedAttentionアルゴリズム: block definition, block table,
+ *    decode equation]
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers are DEVICE pointers unless stated; the caller owns every buffer and
+ * the library never frees or retains them.  All work is enqueued on `stream`
+ * (a hipStream_t passed as void*, NULL = the null stream) and the calls return
+ * without waiting for it.  Calls on one stream are ordered, so
+ * pa_copy_blocks -> pa_write_kv -> pa_decode needs no extra fence.
+ *
+ * Element type `dtype` (pa_dtype): one type for q, caches, new tokens and out.
+ * Arithmetic is fp32 inside the kernels; out is rounded to nearest-even.
+ *
+ * Storage format (B = block_size, D = head_dim, x = 16 / element bytes):
+ *   k_cache  [num_blocks][num_kv_heads][D / x][B][x]
+ *            element (block b, head g, token offset o, dim d) at
+ *            (((b * Hkv + g) * (D / x) + d / x) * B + o) * x + d % x
+ *   v_cache  [num_blocks][num_kv_heads][D][B]
+ *            element (b, g, o, d) at ((b * Hkv + g) * D + d) * B + o
+ *   q, out   [num_seqs][num_heads][D]
+ *   query head h reads kv head h / (num_heads / num_kv_heads).
+ *
+ * Errors: each call returns a pa_status.  Arguments the host can see (sizes,
+ * dtype, null or misaligned pointers) are checked before anything is
+ * enqueued; a failing check enqueues nothing.  Values that live on the device
+ * (slots, block ids, context lengths) are preconditions: the kernels clamp or
+ * skip out-of-range values so that no access leaves the buffers, but the
+ * result for such inputs is unspecified.  pa_last_error() gives a message for
+ * the last failure on the calling thread.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* a size, pointer or dtype the call cannot accept */
+    PA_ERR_UNSUPPORTED = 2, /* valid, but not a shape this build implements */
+    PA_ERR_HIP = 3,         /* the HIP runtime reported an error */
+    PA_ERR_NO_MEMORY = 4    /* the library could not allocate its workspace */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/*
+ * pa_write_kv -- store the keys and values of new tokens in their slots.
+ * A token's slot names a physical block and an offset in it:
+ * slot = block * B + offset (blocks are filled token by token,
+ * [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム, block table example]).
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], device
+ *   k_cache, v_cache  pools in the storage format above, device, updated in place
+ *   slot_mapping   int64 [num_tokens], device.  slot < 0 skips the token.
+ *                  Non-negative slots must be distinct and < num_blocks * B.
+ *
+ * Every element is copied bit for bit; slots not named are left untouched.
+ * Supports head_dim a multiple of x up to 512, any block_size >= 1.
+ * Errors: PA_ERR_INVALID_ARG for non-positive sizes, null pointers, unknown
+ * dtype, head_dim not a multiple of x, or data pointers not 16-byte aligned.
+ */
+int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                const int64_t *slot_mapping, int64_t num_tokens, int num_kv_heads,
+                int head_dim, int block_size, int64_t num_blocks, int dtype, void *stream);
+
+/*
+ * pa_decode -- paged decode attention for one new query token per sequence.
+ *   out[s][h][:] = sum_{i < ctx_s} softmax_i(scale * <q[s][h], k_i>) * v_i
+ * where token i of sequence s sits in physical block block_tables[s][i / B] at
+ * offset i % B.  [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
+ * decode equation; the page fixes scale = 1/sqrt(d), here it is an argument]
+ *
+ *   q              [num_seqs][num_heads][head_dim], device
+ *   k_cache, v_cache  pools (storage format above), device, read only
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq], device; entries at
+ *                  or past ceil(ctx / B) are never read
+ *   context_lens   int32 [num_seqs], device; 0 <= ctx <= max_blocks_per_seq * B.
+ *                  ctx == 0 gives out = 0.  Slots of the last block at or past
+ *                  ctx may hold any bits (NaN included) and do not matter.
+ *   scale          host float, multiplies every dot product
+ *   out            [num_seqs][num_heads][head_dim], device, written
+ *
+ * Long contexts are split into partitions whose partial results are merged
+ * with log-sum-exp weights; the library keeps a grow-only workspace for them
+ * per (device, stream) (PA_ERR_NO_MEMORY if it cannot be allocated).  Results
+ * are bit-identical from run to run and do not depend on where the physical
+ * blocks sit.
+ * Supports block_size 16, head_dim 64 or 128, num_heads a multiple of
+ * num_kv_heads; PA_ERR_UNSUPPORTED otherwise.
+ */
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
+
+/*
+ * pa_decode_ex -- pa_decode with an explicit partition length.
+ *   partition_tokens  0 = choose automatically (what pa_decode does);
+ *                     otherwise a multiple of 16 in [16, 1024]: every
+ *                     sequence is cut into runs of that many tokens, each run
+ *                     is reduced on its own and the runs are merged.  A value
+ *                     >= max_blocks_per_seq * B gives the single-pass kernel.
+ * The split is exact up to rounding: the streaming softmax is associative.
+ *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
+ *    online softmax ("FlashAttention style")]
+ */
+int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                 int partition_tokens, void *stream);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks, the copy step of
+ * copy-on-write: a block shared by several sequences (reference count > 1) is
+ * copied to a fresh block before one of them writes into it.
+ *   [論文解説: PagedAttention, 技術的詳細 › Copy-on-Write KVキャッシュ共有]
+ *
+ *   k_cache, v_cache  pools, device, updated in place
+ *   block_mapping  int64 [num_pairs][2] = (src, dst), device
+ * Copies every kv head, every slot, of K and of V, bit for bit.
+ * Preconditions: ids in [0, num_blocks); destinations distinct; no
+ * destination is also a source in the same call (then the result equals
+ * reading every source before writing any destination).
+ * Errors: PA_ERR_INVALID_ARG for non-positive sizes, null pointers, unknown
+ * dtype or pools not 16-byte aligned.
+ */
+int pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, int64_t num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int64_t num_blocks, int dtype,
+                   void *stream);
+
+/* Name of a status code (static string, never NULL). */
+const char *pa_status_str(int status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *pa_last_error(void);
+
+/* Bytes of workspace pa_decode_ex would use for these sizes (0 = none). */
+int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int partition_tokens);
+
+/* Frees the library-owned decode workspaces after synchronising the device.
+ * Call only when no pa_decode work is pending on any stream. */
+int pa_release_workspaces(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,306 @@
+// pa_api.hip -- the extern "C" entry points of libpa (declared in include/pa.h).
+//
+// Host work per call: check every argument the host can see, plan the launch
+// from host-known sizes only (context lengths stay on the device), make sure
+// the split workspace exists, and enqueue the kernels on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+    return fail(PA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- split workspace: one grow-only buffer per (device, stream) ------------
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int workspace_for(hipStream_t stream, size_t need, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[{dev, stream}];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // the old buffer may still be in use by work queued on this stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        const size_t bytes = need < (size_t)(1 << 20) ? (size_t)(1 << 20) : need;
+        e = hipMalloc(&w.ptr, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            w.ptr = nullptr;
+            return fail(PA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes,
+                        hipGetErrorString(e));
+        }
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return PA_OK;
+}
+
+constexpr int kBlock = 16;
+constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
+constexpr int kMaxPartitions = 1 << 16;
+
+// Partition length when the caller leaves it to the library.  Sequences that
+// fit one partition are finished by one wave; longer ones are split so the
+// launch has enough waves to keep every CU's memory pipeline busy.
+int auto_partition(int num_seqs, int kv_units_per_seq, int max_tokens) {
+    (void)num_seqs;
+    (void)kv_units_per_seq;
+    if (max_tokens <= 256) return 256;
+    return 256;
+}
+
+int64_t num_partitions(int max_tokens, int P) {
+    int64_t np = ((int64_t)max_tokens + P - 1) / P;
+    return np < 1 ? 1 : np;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_str(int status) {
+    switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_NO_MEMORY: return "PA_ERR_NO_MEMORY";
+    default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_version(void) { return 100; }
+
+int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                const int64_t *slot_mapping, int64_t num_tokens, int num_kv_heads, int head_dim,
+                int block_size, int64_t num_blocks, int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_write_kv: unknown dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_write_kv: sizes must be positive (tokens %lld, kv heads %d, head_dim %d, "
+                    "block %d, blocks %lld)",
+                    (long long)num_tokens, num_kv_heads, head_dim, block_size,
+                    (long long)num_blocks);
+    const int x = 16 / e;
+    if (head_dim % x != 0 || head_dim > 512)
+        return fail(PA_ERR_INVALID_ARG, "pa_write_kv: head_dim %d must be a multiple of %d, <= 512",
+                    head_dim, x);
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "pa_write_kv: null pointer");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)slot_mapping & 7u))
+        return fail(PA_ERR_INVALID_ARG, "pa_write_kv: data pointers must be 16-byte aligned");
+    hipError_t err = pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
+                                         num_kv_heads, head_dim, block_size, num_blocks, e,
+                                         (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_write_kv launch");
+    return PA_OK;
+}
+
+int pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, int64_t num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int64_t num_blocks, int dtype,
+                   void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: unknown dtype %d", dtype);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: sizes must be positive");
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * e;
+    if (block_bytes % 16 != 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_copy_blocks: a block of %lld bytes is not a multiple of 16",
+                    (long long)block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_mapping)
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_mapping & 7u))
+        return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pools must be 16-byte aligned");
+    hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
+                                            num_blocks, block_bytes, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_copy_blocks launch");
+    return PA_OK;
+}
+
+int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int partition_tokens) {
+    if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0)
+        return 0;
+    const int max_tokens = max_blocks_per_seq * block_size;
+    int P = partition_tokens > 0 ? partition_tokens : auto_partition(num_seqs, 1, max_tokens);
+    if (P >= max_tokens) return 0;
+    const int64_t np = num_partitions(max_tokens, P);
+    return (int64_t)num_seqs * num_heads * np * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
+int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                 int partition_tokens, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: sizes must be positive");
+    if (num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads %d is not a multiple of %d",
+                    num_heads, num_kv_heads);
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale is not finite");
+    if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % kBlock != 0 ||
+                                                          partition_tokens > kMaxPartition)))
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode: partition_tokens %d must be 0 or a multiple of 16 in [16, 1024]",
+                    partition_tokens);
+    if (block_size != kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (only 16 is built)",
+                    block_size);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (64 and 128 are built)",
+                    head_dim);
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_blocks_per_seq too large");
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: data pointers must be 16-byte aligned");
+
+    const int G = num_heads / num_kv_heads;
+    const int max_tokens = max_blocks_per_seq * kBlock;
+    const bool mfma = dtype != PA_F32 && G >= 2 && G <= 16;
+
+    int P = partition_tokens > 0
+                ? partition_tokens
+                : auto_partition(num_seqs, mfma ? num_kv_heads : num_heads, max_tokens);
+    int64_t NP = 1;
+    if (P < max_tokens) {
+        NP = num_partitions(max_tokens, P);
+    } else {
+        // one partition covers every sequence; keep P a multiple of 16 that does
+        P = max_tokens < kBlock ? kBlock : (max_tokens + kBlock - 1) / kBlock * kBlock;
+        if (P > kMaxPartition) P = kMaxPartition, NP = num_partitions(max_tokens, P);
+    }
+    if (NP > kMaxPartitions)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld partitions (max %d)", (long long)NP,
+                    kMaxPartitions);
+    const int64_t units = NP * (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads);
+    if (units > (int64_t)0x7fffffff - 4096)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work units", (long long)units);
+
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.bt = block_tables;
+    a.ctx = context_lens;
+    a.out = out;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.S = num_seqs;
+    a.Hq = num_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.MB = max_blocks_per_seq;
+    a.NP = (int)NP;
+    a.P = P;
+    a.NB = num_blocks;
+    a.num_units = (int)units;
+    a.run = mfma ? 1 : 8;
+    if (NP > 1) {
+        void *ws = nullptr;
+        const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
+        const size_t ml_bytes = (size_t)num_seqs * num_heads * NP * 2 * sizeof(float);
+        int rc = workspace_for((hipStream_t)stream, o_bytes + ml_bytes, &ws);
+        if (rc != PA_OK) return rc;
+        a.part_o = (float *)ws;
+        a.part_ml = (float *)((char *)ws + o_bytes);
+    }
+    hipError_t err = pa::launch_decode(a, dtype, head_dim,
+                                       mfma ? pa::DecodeKernel::kMfma : pa::DecodeKernel::kValu,
+                                       (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_decode launch");
+    return PA_OK;
+}
+
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream) {
+    return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                        num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, dtype, 0, stream);
+}
+
+int pa_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int rc = PA_OK;
+    for (auto &kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        int prev = 0;
+        (void)hipGetDevice(&prev);
+        (void)hipSetDevice(kv.first.first);
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        if (e != hipSuccess) rc = hip_fail(e, "pa_release_workspaces");
+        (void)hipSetDevice(prev);
+        kv.second = Workspace{};
+    }
+    g_ws.clear();
+    return rc;
+}
+
+}  // extern "C"

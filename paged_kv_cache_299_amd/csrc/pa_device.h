@@ -1,0 +1,99 @@
+// pa_device.h -- device-side helpers shared by the libpa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Element type codes, same numbering as pa_dtype in include/pa.h.
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { static constexpr int bytes = 4; };
+template <> struct Elem<kF16> { static constexpr int bytes = 2; };
+template <> struct Elem<kBF16> { static constexpr int bytes = 2; };
+
+// ---- 16-bit <-> fp32 -----------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <int DT> __device__ __forceinline__ float elem_lo(uint32_t w) {
+    return DT == kBF16 ? bf16_lo(w) : f16_lo(w);
+}
+template <int DT> __device__ __forceinline__ float elem_hi(uint32_t w) {
+    return DT == kBF16 ? bf16_hi(w) : f16_hi(w);
+}
+
+// fp32 -> 16-bit bits, round to nearest even (NaN stays NaN).
+template <int DT> __device__ __forceinline__ uint16_t to_bits16(float f) {
+    if constexpr (DT == kBF16) {
+        return __builtin_bit_cast(uint16_t, (__bf16)f);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    }
+}
+
+// ---- cross-lane ------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+// Maximum / sum over the 16 lanes of a row (lanes 16r .. 16r+15), result in all of them.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, shfl_xor(v, 1));
+    v = fmaxf(v, shfl_xor(v, 2));
+    v = fmaxf(v, shfl_xor(v, 4));
+    v = fmaxf(v, shfl_xor(v, 8));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += shfl_xor(v, 1);
+    v += shfl_xor(v, 2);
+    v += shfl_xor(v, 4);
+    v += shfl_xor(v, 8);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- loads -----------------------------------------------------------------
+__device__ __forceinline__ i32x4 ld16(const void *p) { return *(const i32x4 *)p; }
+__device__ __forceinline__ i32x2 ld8(const void *p) { return *(const i32x2 *)p; }
+// Streaming loads for K/V tiles, each read once per decode: the nontemporal
+// hint keeps them from displacing reusable lines (measured on MI355X: random
+// 4 KiB tile reads go from ~5.7 to ~6.4 TB/s with it).
+__device__ __forceinline__ i32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load((const i32x4 *)p);
+}
+__device__ __forceinline__ i32x2 ld8_stream(const void *p) {
+    return __builtin_nontemporal_load((const i32x2 *)p);
+}
+
+// Workgroups go to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).
+// Map workgroup b to logical unit u so that every XCD takes runs of `run`
+// consecutive units: XCD x gets [r*8*run + x*run, r*8*run + (x+1)*run) for
+// r = 0, 1, ...  Units next to each other in logical order then share an L2.
+__device__ __forceinline__ int xcd_unit(int b, int run) {
+    const int x = b & 7;
+    const int k = b >> 3;
+    return (k / run) * 8 * run + x * run + (k % run);
+}
+
+}  // namespace pa

@@ -1,0 +1,39 @@
+// pa_internal.h -- host-side declarations shared by the libpa translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one decode launch needs; passed by value as the kernel argument.
+struct DecodeArgs {
+    const void *q;          // [S][Hq][D]
+    const void *k;          // K pool [NB][Hkv][D/x][B][x]
+    const void *v;          // V pool [NB][Hkv][D][B]
+    const int *bt;          // [S][MB]
+    const int *ctx;         // [S]
+    void *out;              // [S][Hq][D]
+    float *part_o;          // [S][Hq][NP][D]   (split path only)
+    float *part_ml;         // [S][Hq][NP][2]   (m in log2 units, l)
+    float scale_log2;       // scale * log2(e)
+    int S, Hq, Hkv, G, MB, NP, P;
+    int64_t NB;
+    int num_units;          // logical work units of the launch
+    int run;                // XCD run length (see xcd_unit)
+};
+
+enum class DecodeKernel { kValu, kMfma };
+
+// Launch the partition kernel (and, when NP > 1, the merge kernel).
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, DecodeKernel kind,
+                         hipStream_t stream);
+
+hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
+                           int elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t n,
+                              int64_t NB, int64_t block_bytes, hipStream_t stream);
+
+}  // namespace pa

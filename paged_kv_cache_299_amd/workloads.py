@@ -118,66 +118,73 @@ def _tables(bm: BlockManager, seq_ids, MB: int) -> torch.Tensor:
 def make_decode_case(name: str, *, seed: int, context_lens: Sequence[int], num_heads: int,
                      num_kv_heads: int, head_dim: int, block_size: int, num_blocks: int,
                      max_blocks: int, dtype: torch.dtype, partition_tokens: Optional[int] = None,
-                     rng: Optional[np.random.Generator] = None) -> DecodeCase:
-    """One decode step for independent sequences: write token ctx-1, attend over ctx."""
+                     rng: Optional[np.random.Generator] = None, fill: bool = True) -> DecodeCase:
+    """One decode step for independent sequences: write token ctx-1, attend over ctx.
+
+    A sequence with ctx 0 holds nothing and gets no new token (slot -1)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     S = len(context_lens)
     B = block_size
     ctx = [int(c) for c in context_lens]
-    if any(c < 1 for c in ctx):
-        raise ValueError("a decode step needs ctx >= 1 (the new token)")
+    if any(c < 0 for c in ctx):
+        raise ValueError("context lengths must be >= 0")
     if any(-(-c // B) > max_blocks for c in ctx):
         raise ValueError("a context does not fit max_blocks")
     bm = BlockManager(num_blocks, B, free_order=rng.permutation(num_blocks))
     for s in range(S):
-        bm.allocate(s, ctx[s] - 1)
-    k, v = _fill_pools(rng, bm, range(S), num_kv_heads, head_dim, B, num_blocks, dtype)
+        bm.allocate(s, max(ctx[s] - 1, 0))
+    k, v = (_fill_pools(rng, bm, range(S), num_kv_heads, head_dim, B, num_blocks, dtype)
+            if fill else (None, None))
     q = _randn(rng, (S, num_heads, head_dim), dtype)
-    slots = [bm.append_slot(s)[0] for s in range(S)]
+    # an empty sequence (ctx 0) gets no new token: slot -1 is skipped by the write
+    slots = [bm.append_slot(s)[0] if ctx[s] > 0 else -1 for s in range(S)]
     step = WriteStep(_randn(rng, (S, num_kv_heads, head_dim), dtype),
                      _randn(rng, (S, num_kv_heads, head_dim), dtype),
                      torch.tensor(slots, dtype=torch.int64))
-    return DecodeCase(name, dtype, S, num_heads, num_kv_heads, head_dim, B, num_blocks,
+    case = DecodeCase(name, dtype, S, num_heads, num_kv_heads, head_dim, B, num_blocks,
                       max_blocks, q, k, v, _tables(bm, range(S), max_blocks),
                       torch.tensor(ctx, dtype=torch.int32), 1.0 / math.sqrt(head_dim),
                       [step], partition_tokens, seed)
+    case.block_manager = bm
+    return case
 
 
-def tiny(seed: int = 1) -> DecodeCase:
+def tiny(seed: int = 1, fill: bool = True) -> DecodeCase:
     """1 seq, 1 head, D 64, ctx 100 -> write token 100 -> ctx 101, fp32, 16 blocks."""
     return make_decode_case("tiny", seed=seed, context_lens=[101], num_heads=1, num_kv_heads=1,
                             head_dim=64, block_size=16, num_blocks=16, max_blocks=7,
-                            dtype=torch.float32)
+                            dtype=torch.float32, fill=fill)
 
 
-def llama3_8b(seed: int = 2, num_seqs: int = 32) -> DecodeCase:
+def llama3_8b(seed: int = 2, num_seqs: int = 32, fill: bool = True) -> DecodeCase:
     rng = np.random.default_rng(seed)
     ctx = rng.integers(128, 4096, size=num_seqs, endpoint=True)
     return make_decode_case("llama3_8b", seed=seed, context_lens=ctx, num_heads=32,
                             num_kv_heads=8, head_dim=128, block_size=16, num_blocks=12000,
-                            max_blocks=256, dtype=torch.bfloat16, rng=rng)
+                            max_blocks=256, dtype=torch.bfloat16, rng=rng, fill=fill)
 
 
-def opt_13b(seed: int = 3, num_seqs: int = 64) -> DecodeCase:
+def opt_13b(seed: int = 3, num_seqs: int = 64, fill: bool = True) -> DecodeCase:
     rng = np.random.default_rng(seed)
     z = rng.standard_normal(num_seqs)
     ctx = np.clip(np.rint(512.0 * np.exp(z)), 16, 2048).astype(np.int64)
     return make_decode_case("opt_13b", seed=seed, context_lens=ctx, num_heads=40,
                             num_kv_heads=40, head_dim=128, block_size=16, num_blocks=10000,
-                            max_blocks=128, dtype=torch.float16, rng=rng)
+                            max_blocks=128, dtype=torch.float16, rng=rng, fill=fill)
 
 
-def long_ctx(seed: int = 5) -> DecodeCase:
+def long_ctx(seed: int = 5, fill: bool = True) -> DecodeCase:
     ctx = [32768, 65536, 98304, 131072]
     return make_decode_case("long_ctx", seed=seed, context_lens=ctx, num_heads=32,
                             num_kv_heads=8, head_dim=128, block_size=16, num_blocks=24576,
-                            max_blocks=8192, dtype=torch.bfloat16, partition_tokens=512)
+                            max_blocks=8192, dtype=torch.bfloat16, partition_tokens=512,
+                            fill=fill)
 
 
 def parallel_sampling(seed: int = 4, cow: bool = False, num_prompts: int = 16,
                       samples: int = 8, prompt_tokens: Optional[int] = None,
                       max_private: int = 256, num_heads: int = 32, head_dim: int = 128,
-                      num_blocks: int = 4096) -> DecodeCase:
+                      num_blocks: int = 4096, fill: bool = True) -> DecodeCase:
     """Parallel sampling over shared prompt blocks.
 
     Sequence id = prompt * samples + sample.  Sample 0 holds the prompt, the
@@ -205,7 +212,8 @@ def parallel_sampling(seed: int = 4, cow: bool = False, num_prompts: int = 16,
         bm.allocate(p * samples, P)
         for j in range(1, samples):
             bm.fork(p * samples, p * samples + j)
-    k, v = _fill_pools(rng, bm, range(S), Hkv, head_dim, B, num_blocks, torch.bfloat16)
+    k, v = (_fill_pools(rng, bm, range(S), Hkv, head_dim, B, num_blocks, torch.bfloat16)
+            if fill else (None, None))
     q = _randn(rng, (S, num_heads, head_dim), torch.bfloat16)
     steps: List[object] = []
     first_slots: List[int] = []
@@ -244,7 +252,7 @@ CASES = {
     "tiny": tiny,
     "llama3_8b": llama3_8b,
     "opt_13b": opt_13b,
-    "parallel_sampling": lambda: parallel_sampling(cow=False),
-    "parallel_sampling_cow": lambda: parallel_sampling(cow=True),
+    "parallel_sampling": lambda **kw: parallel_sampling(cow=False, **kw),
+    "parallel_sampling_cow": lambda **kw: parallel_sampling(cow=True, **kw),
     "long_ctx": long_ctx,
 }

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports what include/pa.h
+declares, and rejects bad host-visible arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_299_amd as pa
+from paged_kv_cache_299_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+BF16, F16, F32 = 2, 1, 0
+ALIGNED = ctypes.c_void_p(1 << 20)   # never dereferenced: checks fail before any launch
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pa.load_library()
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = pa.load_library()
+    assert pa.pa_status_str(OK) == "PA_OK"
+    assert pa.pa_status_str(INVALID) == "PA_ERR_INVALID_ARG"
+    assert pa.pa_status_str(99) == "PA_ERR_UNKNOWN"
+    assert lib.pa_version() >= 100
+
+
+def _decode(lib, **kw):
+    args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, bt=ALIGNED, ctx=ALIGNED, scale=0.1, out=ALIGNED,
+                S=4, Hq=32, Hkv=8, D=128, B=16, MB=16, NB=100, dtype=BF16, P=0, stream=None)
+    args.update(kw)
+    return lib.pa_decode_ex(args["q"], args["k"], args["v"], args["bt"], args["ctx"],
+                            args["scale"], args["out"], args["S"], args["Hq"], args["Hkv"],
+                            args["D"], args["B"], args["MB"], args["NB"], args["dtype"], args["P"],
+                            args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(Hkv=0), INVALID),
+    (dict(NB=0), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(P=20), INVALID),
+    (dict(P=2048), INVALID),
+    (dict(B=32), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(q=None), INVALID),
+    (dict(out=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+    (dict(S=0), OK),
+])
+def test_decode_argument_checks(kw, status):
+    lib = pa.load_library()
+    assert _decode(lib, **kw) == status
+    if status != OK:
+        assert lib.pa_last_error().decode()
+
+
+def test_write_and_copy_argument_checks():
+    lib = pa.load_library()
+    A = ALIGNED
+    assert lib.pa_write_kv(A, A, A, A, A, 0, 8, 128, 16, 10, BF16, None) == OK
+    assert lib.pa_write_kv(A, A, A, A, A, 5, 8, 12, 16, 10, BF16, None) == INVALID  # 12 % 8
+    assert lib.pa_write_kv(A, A, A, A, A, 5, 8, 128, 16, 10, 9, None) == INVALID
+    assert lib.pa_write_kv(None, A, A, A, A, 5, 8, 128, 16, 10, BF16, None) == INVALID
+    assert lib.pa_copy_blocks(A, A, A, 0, 8, 128, 16, 10, BF16, None) == OK
+    assert lib.pa_copy_blocks(A, A, None, 3, 8, 128, 16, 10, BF16, None) == INVALID
+    assert lib.pa_copy_blocks(A, A, A, -1, 8, 128, 16, 10, BF16, None) == INVALID
+
+
+def test_workspace_size_query():
+    lib = pa.load_library()
+    # 32 seqs x 32 heads x ceil(4096/256) partitions x (128 + 2) floats
+    assert lib.pa_decode_workspace_bytes(32, 32, 128, 16, 256, 256) == 32 * 32 * 16 * 130 * 4
+    assert lib.pa_decode_workspace_bytes(32, 32, 128, 16, 8, 256) == 0   # one partition
+    assert lib.pa_decode_workspace_bytes(0, 32, 128, 16, 8, 256) == 0
+
+
+def test_python_binding_maps_invalid_arguments_to_value_error():
+    import torch
+    k = torch.zeros(4, 2, 16, 16, 8, dtype=torch.bfloat16)
+    v = torch.zeros(4, 2, 128, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.pa_decode(torch.zeros(1, 3, 128, dtype=torch.bfloat16), k, v,
+                     torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                     0.1, torch.zeros(1, 3, 128, dtype=torch.bfloat16))
