@@ -87,13 +87,19 @@ constexpr int kBlock = 16;
 constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
 constexpr int kMaxPartitions = 1 << 16;
 
-// Partition length when the caller leaves it to the library.  Sequences that
-// fit one partition are finished by one wave; longer ones are split so the
-// launch has enough waves to keep every CU's memory pipeline busy.
-int auto_partition(int num_seqs, int kv_units_per_seq, int max_tokens) {
-    (void)num_seqs;
-    (void)kv_units_per_seq;
-    if (max_tokens <= 256) return 256;
+// Partition length when the caller leaves it to the library.  A grouped-query
+// unit (one kv head, G query heads on MFMA) streams its tiles fastest in long
+// runs, so take the longest of 1024 / 512 tokens that still gives at least
+// four units per compute unit when every sequence is as long as the table
+// allows (the host cannot see the real lengths); one-head units on VALU do
+// more work per byte and prefer 256-token runs.
+int auto_partition(bool mfma, int64_t pairs, int max_tokens) {
+    constexpr int64_t kMinUnits = 4 * 256;
+    if (mfma) {
+        for (int P : {1024, 512}) {
+            if (pairs * (((int64_t)max_tokens + P - 1) / P) >= kMinUnits) return P;
+        }
+    }
     return 256;
 }
 
@@ -180,7 +186,8 @@ int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int
         max_blocks_per_seq <= 0)
         return 0;
     const int max_tokens = max_blocks_per_seq * block_size;
-    int P = partition_tokens > 0 ? partition_tokens : auto_partition(num_seqs, 1, max_tokens);
+    // an upper bound: the smallest partition length the library picks itself
+    int P = partition_tokens > 0 ? partition_tokens : 256;
     if (P >= max_tokens) return 0;
     const int64_t np = num_partitions(max_tokens, P);
     return (int64_t)num_seqs * num_heads * np * (head_dim + 2) * (int64_t)sizeof(float);
@@ -226,7 +233,8 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
 
     int P = partition_tokens > 0
                 ? partition_tokens
-                : auto_partition(num_seqs, mfma ? num_kv_heads : num_heads, max_tokens);
+                : auto_partition(mfma, (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
+                                 max_tokens);
     int64_t NP = 1;
     if (P < max_tokens) {
         NP = num_partitions(max_tokens, P);
@@ -259,7 +267,8 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     a.P = P;
     a.NB = num_blocks;
     a.num_units = (int)units;
-    a.run = mfma ? 1 : 8;
+    a.run = 1;
+    a.waves_per_unit = 1;
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);

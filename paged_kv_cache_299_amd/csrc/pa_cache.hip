@@ -9,9 +9,13 @@
 
 namespace pa {
 
-// One thread per (token, kv head, 16-byte run of the head vector).  The K run
-// of x dims lands as one 16-byte store in the [D/x][B][x] tile; the same run
-// of V is x separate elements, one per dim row of the [D][B] tile.
+// A 256-thread workgroup stores a tile of TT consecutive tokens of one kv
+// head, TT = 256 / (16-byte runs per head vector).  Each thread loads one
+// 16-byte run of K and of V.  The K run is one 16-byte store into the
+// [D/x][B][x] tile.  V is transposed in the pool ([D][B] per tile), so the
+// runs go through LDS and are stored element by element with the token as
+// the fastest lane index: when consecutive tokens go to consecutive slots
+// (prompt fill, appends) 16 lanes write one contiguous 16-slot row segment.
 template <int E>
 __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ k_new,
                                                        const char *__restrict__ v_new,
@@ -21,32 +25,61 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
                                                        int64_t num_tokens, int Hkv, int D, int B,
                                                        int64_t num_slots) {
     constexpr int X = 16 / E;
-    const int NC = D / X;
-    const int64_t total = num_tokens * Hkv * NC;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)(idx % NC);
-        const int64_t rest = idx / NC;
-        const int g = (int)(rest % Hkv);
-        const int64_t t = rest / Hkv;
-        const int64_t slot = slots[t];
-        if (slot < 0 || slot >= num_slots) continue;  // padding, or out of range
+    // TT rows of D*E/4 words plus one pad word each: TT * D*E/4 <= 1024 and TT <= 256
+    __shared__ uint32_t vtile[1024 + 256];
+    __shared__ int64_t slot_sh[256];
+    const int NC = D / X;        // 16-byte runs per head vector (1..128)
+    const int TT = 256 / NC;     // tokens per tile
+    const int tid = threadIdx.x;
+    const int g = blockIdx.y;
+    const int64_t t_base = (int64_t)blockIdx.x * TT;
+    // row stride in 32-bit words: one pad word, so that reading one dim of
+    // consecutive tokens walks different LDS banks
+    const int row_words = D * E / 4 + 1;
+
+    // 1. loads: thread -> (token tt, run c)
+    const int tt = tid / NC, c = tid % NC;
+    const int64_t t = t_base + tt;
+    int64_t slot = -1;
+    i32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+    if (tt < TT && t < num_tokens) {
+        const int64_t src = ((t * Hkv + g) * D) * E + (int64_t)c * 16;
+        slot = slots[t];
+        kv = ld16(k_new + src);
+        vv = ld16(v_new + src);
+    }
+    const bool ok = slot >= 0 && slot < num_slots;
+    if (ok) {
         const int64_t blk = slot / B;
         const int off = (int)(slot % B);
-        const int64_t src = ((t * Hkv + g) * D) * E + (int64_t)c * 16;
         const int64_t tile = (blk * Hkv + g) * (int64_t)D * B;  // elements
-        const i32x4 kv = ld16(k_new + src);
         *(i32x4 *)(k_cache + (tile + ((int64_t)c * B + off) * X) * E) = kv;
-        const i32x4 vv = ld16(v_new + src);
-        const char *vb = (const char *)&vv;
-#pragma unroll
-        for (int e = 0; e < X; ++e) {
-            char *dst = v_cache + (tile + (int64_t)(c * X + e) * B + off) * E;
-            if constexpr (E == 4) {
-                *(uint32_t *)dst = *(const uint32_t *)(vb + 4 * e);
-            } else {
-                *(uint16_t *)dst = *(const uint16_t *)(vb + 2 * e);
-            }
+    }
+    if (tt < TT) {
+        if (c == 0) slot_sh[tt] = slot;
+        uint32_t *row = vtile + tt * row_words + c * 4;
+        row[0] = (uint32_t)vv[0];
+        row[1] = (uint32_t)vv[1];
+        row[2] = (uint32_t)vv[2];
+        row[3] = (uint32_t)vv[3];
+    }
+    __syncthreads();
+    // 2. V stores: element e -> (token e % TT, dim e / TT)
+    const int64_t tiles_left = num_tokens - t_base;
+    const int ntok = tiles_left < TT ? (int)tiles_left : TT;
+    for (int e = tid; e < TT * D; e += 256) {
+        const int et = e % TT, d = e / TT;
+        if (et >= ntok) continue;
+        const int64_t sl = slot_sh[et];
+        if (sl < 0 || sl >= num_slots) continue;
+        const int64_t blk = sl / B;
+        const int off = (int)(sl % B);
+        char *dst = v_cache + (((blk * Hkv + g) * D + d) * (int64_t)B + off) * E;
+        const char *src = (const char *)(vtile + et * row_words) + d * E;
+        if constexpr (E == 4) {
+            *(uint32_t *)dst = *(const uint32_t *)src;
+        } else {
+            *(uint16_t *)dst = *(const uint16_t *)src;
         }
     }
 }
@@ -78,18 +111,18 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char *__restrict__ k_c
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
                            int elem_bytes, hipStream_t stream) {
-    const int X = 16 / elem_bytes;
-    const int64_t total = T * Hkv * (D / X);
-    if (total == 0) return hipSuccess;
-    const int threads = 256;
-    int64_t blocks = (total + threads - 1) / threads;
-    if (blocks > 65536) blocks = 65536;
+    if (T == 0) return hipSuccess;
+    const int NC = D * elem_bytes / 16;  // <= 64 (head_dim <= 512 at 2 bytes, 256 at 4)
+    const int TT = 256 / NC;
+    const int64_t tiles = (T + TT - 1) / TT;
+    if (tiles > 0x7fffffff || Hkv > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles, (unsigned)Hkv);
     if (elem_bytes == 4) {
-        write_kv_kernel<4><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+        write_kv_kernel<4><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
             Hkv, D, B, NB * B);
     } else {
-        write_kv_kernel<2><<<dim3((unsigned)blocks), dim3(threads), 0, stream>>>(
+        write_kv_kernel<2><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
             Hkv, D, B, NB * B);
     }

@@ -19,9 +19,10 @@
 //  * decode_mfma_kernel (bf16/fp16, 2..16 query heads per kv head): the G
 //    query heads of one kv head form a small dense contraction.  Per block of
 //    16 tokens: S^T[16 tok x 16 heads] = K[16 x D] . Q^T on
-//    v_mfma_f32_16x16x32 (heads padded to 16), then O^T[D x 16] += V^T[D x 16
-//    tok] . P^T on v_mfma_f32_16x16x16, with P split into a high and a low
-//    16-bit part so the weights keep ~16 significant bits.
+//    v_mfma_f32_16x16x32 (heads padded to 16); per pair of blocks:
+//    O^T[D x 16] += V^T[D x 32 tok] . P^T, again on v_mfma_f32_16x16x32, with
+//    P split into a high and a low 16-bit part so the weights keep ~16
+//    significant bits.
 //  * decode_valu_kernel (one query head per unit; fp32, or G == 1): dot
 //    products with v_dot2 / FMA on 16-byte loads, cross-lane reductions, and
 //    P.V with the 16 weights broadcast through SGPRs.
@@ -42,27 +43,18 @@ namespace pa {
 constexpr int kB = 16;  // tokens per block (the only block size these kernels take)
 
 // ---------------------------------------------------------------------------
-// MFMA operand helpers
+// MFMA helper: D = A . B + C on v_mfma_f32_16x16x32 (bf16 or f16).  Lane l
+// supplies A[l % 16][8 (l / 16) .. +8] and B[8 (l / 16) .. +8][l % 16] and
+// receives D[4 (l / 16) .. +4][l % 16] (checked on the hardware).
 // ---------------------------------------------------------------------------
 template <int DT>
-__device__ __forceinline__ f32x4 mfma_qk(const i32x4 &a, const i32x4 &b, const f32x4 &c) {
+__device__ __forceinline__ f32x4 mfma32(const i32x4 &a, const i32x4 &b, const f32x4 &c) {
     if constexpr (DT == kBF16) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     } else {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ f32x4 mfma_pv(const i32x2 &a, const i32x2 &b, const f32x4 &c) {
-    if constexpr (DT == kBF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
     }
 }
 
@@ -115,8 +107,8 @@ __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c
 // 4j..4j+3] (8 bytes of the [D][16] V tile), and whose result O^T[dims 16t +
 // 4j..4j+3][head n] stays in the lane across blocks.
 // ---------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+template <int DT, int D, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
@@ -124,16 +116,21 @@ void decode_mfma_kernel(const DecodeArgs a) {
     constexpr int NVT = D / 16;       // P.V output tiles, 16 dims each
     constexpr int TILE = D * kB * 2;  // bytes of one (block, kv head) tile
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;  // wave of the unit: it takes block pairs wv, wv + W, ...
     const int n = lane & 15;
     const int j = lane >> 4;
 
+    // Unit order (partition, sequence, kv head), head fastest: workgroup b runs
+    // on XCD b % 8, so with a multiple of 8 kv heads every XCD gets one head of
+    // every (sequence, partition) and the same share of work whatever the
+    // context lengths (sequence-fastest order tied each XCD to fixed sequences).
     int u = xcd_unit(blockIdx.x, a.run);
     if (u >= a.num_units) return;
-    const int s = u % a.S;
-    u /= a.S;
     const int g = u % a.Hkv;
-    const int p = u / a.Hkv;
+    u /= a.Hkv;
+    const int s = u % a.S;
+    const int p = u / a.S;
 
     const int t0 = p * a.P;
     const int blk0 = t0 / kB;
@@ -173,82 +170,189 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < NVT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4 kf[NKC];
-    i32x2 vf[NVT];
+    // K operand slices of a pair of blocks, and V operand slices of a pair.
+    struct KRegs {
+        i32x4 a[NKC], b[NKC];
+    };
+    struct VRegs {
+        i32x2 a[NVT], b[NVT];
+    };
+    KRegs kr;
+    VRegs v0, v1;
 
-    auto load_k = [&](int i) {
-        const char *kt = kbase + (int64_t)__builtin_amdgcn_readlane(my_bt, i) * blk_stride;
+    // Valid tokens of block b of the unit (16 except in its last block).
+    auto valid = [&](int b) {
+        const int v = t1 - (t0 + b * kB);
+        return v < 0 ? 0 : (v > kB ? kB : v);
+    };
+    // Second block of pair q; an absent one (odd block count) re-reads the
+    // first block's tile and is masked out, so every pair issues the same loads.
+    auto second = [&](int q) { return min(2 * q + 1, nblk - 1); };
+
+    auto load_k = [&](int q) {
+        const char *ka = kbase + (int64_t)__builtin_amdgcn_readlane(my_bt, 2 * q) * blk_stride;
+        const char *kb = kbase + (int64_t)__builtin_amdgcn_readlane(my_bt, second(q)) * blk_stride;
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) kf[c] = ld16_stream(kt + (64 * c + lane) * 16);
+        for (int c = 0; c < NKC; ++c) kr.a[c] = ld16_stream(ka + (64 * c + lane) * 16);
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) kr.b[c] = ld16_stream(kb + (64 * c + lane) * 16);
         issue_point();
     };
-    auto load_v = [&](int i) {
-        const char *vt = vbase + (int64_t)__builtin_amdgcn_readlane(my_bt, i) * blk_stride;
+    auto load_v = [&](VRegs &r, int q) {
+        const char *va = vbase + (int64_t)__builtin_amdgcn_readlane(my_bt, 2 * q) * blk_stride;
+        const char *vb = vbase + (int64_t)__builtin_amdgcn_readlane(my_bt, second(q)) * blk_stride;
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) vf[t] = ld8_stream(vt + ((16 * t + n) * kB + 4 * j) * 2);
+        for (int t = 0; t < NVT; ++t) r.a[t] = ld8_stream(va + ((16 * t + n) * kB + 4 * j) * 2);
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) r.b[t] = ld8_stream(vb + ((16 * t + n) * kB + 4 * j) * 2);
         issue_point();
     };
-    auto scores = [&]() {
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // Scores of both blocks of the pair in kr.
+    auto scores = [&](f32x4 &sa, f32x4 &sb) {
+        sa = f32x4{0.f, 0.f, 0.f, 0.f};
+        sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) sc = mfma_qk<DT>(kf[c], qf[c], sc);
-        return sc;
+        for (int c = 0; c < NKC; ++c) {
+            sa = mfma32<DT>(kr.a[c], qf[c], sa);
+            sb = mfma32<DT>(kr.b[c], qf[c], sb);
+        }
     };
-    // Online-softmax update and P.V for one block with nv valid tokens (16
-    // except in the unit's last block, the only one that can be partial).
-    auto update = [&](const f32x4 &sc, int nv, bool tail) {
-        float sv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sv[e] = (!tail || 4 * j + e < nv) ? sc[e] * a.scale_log2 : -INFINITY;
-        float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        bm = fmaxf(bm, shfl_xor(bm, 16));
-        bm = fmaxf(bm, shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        float pe[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(sv[e] - mn);
-        l = l * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-        // P = hi + lo, both 16-bit: hi = RNE(p), lo = RNE(p - hi).
-        uint32_t hb[4], lb[4];
+    // Mask of the 16-bit V elements of tokens 4j..4j+3 that are valid (< nv).
+    auto vmask = [&](int nv, uint32_t &m0, uint32_t &m1) {
+        m0 = (4 * j + 0 < nv ? 0x0000ffffu : 0u) | (4 * j + 1 < nv ? 0xffff0000u : 0u);
+        m1 = (4 * j + 2 < nv ? 0x0000ffffu : 0u) | (4 * j + 3 < nv ? 0xffff0000u : 0u);
+    };
+    // One online-softmax step over a pair of blocks A (nva valid tokens) and B
+    // (nvb valid).  P.V runs on v_mfma_f32_16x16x32: lane group j supplies the
+    // k-slots 8j..8j+7 = tokens 4j..4j+3 of A, then of B, which is both how its
+    // two 8-byte V slices concatenate and how its two sets of four scores do.
+    // Empty slots (only in the unit's last pair) are masked: score -inf, V
+    // zeroed (they may hold NaN).
+    //
+    // The reference maximum m moves only when a lane's block maximum exceeds it
+    // by more than 8 (a factor 2^8): weights exp2(s - m) then stay <= 256, and
+    // the rescale of O and l by exp2(m_old - m_new) is skipped for most steps.
+    auto update2 = [&](const VRegs &V, const f32x4 &sa, const f32x4 &sb, int nva, int nvb,
+                       bool mask) {
+        float sv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            sv[e] = (!mask || 4 * j + e < nva) ? sa[e] * a.scale_log2 : -INFINITY;
+            sv[4 + e] = (!mask || 4 * j + e < nvb) ? sb[e] * a.scale_log2 : -INFINITY;
+        }
+        float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        bm = xor32_max(xor16_max(bm));
+        const bool grow = bm > m + 8.f;
+        if (__any(grow)) {
+            const float mn = grow ? bm : m;
+            const float alpha = fast_exp2(m - mn);  // 0 on the first step (m = -inf)
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) o[t] *= alpha;
+            l *= alpha;
+            m = mn;
+        }
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sv[e] - m);
+        l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        // P = hi + lo, both 16-bit: hi = RNE(p), lo = RNE(p - hi).
+        uint32_t hb[8], lb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
             hb[e] = to_bits16<DT>(pe[e]);
             lb[e] = to_bits16<DT>(pe[e] - from_bits16<DT>(hb[e]));
         }
-        const i32x2 phi = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16))};
-        const i32x2 plo = {(int)(lb[0] | (lb[1] << 16)), (int)(lb[2] | (lb[3] << 16))};
-        uint32_t mask0 = 0xffffffffu, mask1 = 0xffffffffu;
-        if (tail) {  // empty slots of the last block may hold any bits (NaN): zero their V
-            mask0 = (4 * j + 0 < nv ? 0x0000ffffu : 0u) | (4 * j + 1 < nv ? 0xffff0000u : 0u);
-            mask1 = (4 * j + 2 < nv ? 0x0000ffffu : 0u) | (4 * j + 3 < nv ? 0xffff0000u : 0u);
+        const i32x4 phi = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16)),
+                           (int)(hb[4] | (hb[5] << 16)), (int)(hb[6] | (hb[7] << 16))};
+        const i32x4 plo = {(int)(lb[0] | (lb[1] << 16)), (int)(lb[2] | (lb[3] << 16)),
+                           (int)(lb[4] | (lb[5] << 16)), (int)(lb[6] | (lb[7] << 16))};
+        uint32_t ma0 = 0xffffffffu, ma1 = 0xffffffffu, mb0 = 0xffffffffu, mb1 = 0xffffffffu;
+        if (mask) {
+            vmask(nva, ma0, ma1);
+            vmask(nvb, mb0, mb1);
         }
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
-            const i32x2 vv = {(int)((uint32_t)vf[t][0] & mask0), (int)((uint32_t)vf[t][1] & mask1)};
-            o[t] *= alpha;
-            o[t] = mfma_pv<DT>(vv, phi, o[t]);
-            o[t] = mfma_pv<DT>(vv, plo, o[t]);
+            const i32x4 vv = {(int)((uint32_t)V.a[t][0] & ma0), (int)((uint32_t)V.a[t][1] & ma1),
+                              (int)((uint32_t)V.b[t][0] & mb0), (int)((uint32_t)V.b[t][1] & mb1)};
+            o[t] = mfma32<DT>(vv, phi, o[t]);
+            o[t] = mfma32<DT>(vv, plo, o[t]);
         }
     };
+    auto last_step = [&](const VRegs &V, int q) {
+        f32x4 sa, sb;
+        scores(sa, sb);
+        update2(V, sa, sb, valid(2 * q), 2 * q + 1 < nblk ? valid(2 * q + 1) : 0, true);
+    };
 
-    load_k(0);
-    load_v(0);
-    for (int i = 0; i < nblk - 1; ++i) {  // every block but the last is full
-        const f32x4 sc = scores();
-        load_k(i + 1);
-        update(sc, kB, false);
-        load_v(i + 1);
-    }
-    {
-        const f32x4 sc = scores();
-        update(sc, t1 - (t0 + (nblk - 1) * kB), true);
+    // Pairs of this wave: q = wv, wv + W, ...  One K register set and two V
+    // sets: right after the scores of pair q consume K, both K and V of the
+    // wave's next pair are requested (V into the other set), so a whole pair
+    // is in flight while pair q is reduced.  The loop is unrolled by two so the
+    // V sets alternate without copies, and issues its loads without conditions
+    // so the wait counts stay exact; the wave's last pair is masked.
+    const int npairs = (nblk + 1) / 2;
+    const int nk = npairs > wv ? (npairs - wv + W - 1) / W : 0;  // pairs of this wave
+    if (nk > 0) {
+        int q = wv;
+        int k = 0;
+        load_k(q);
+        load_v(v0, q);
+        for (; k + 2 < nk; k += 2, q += 2 * W) {  // pairs q, q + W full; q + 2W exists
+            f32x4 sa, sb;
+            scores(sa, sb);
+            load_k(q + W);
+            load_v(v1, q + W);
+            update2(v0, sa, sb, kB, kB, false);
+            scores(sa, sb);
+            load_k(q + 2 * W);
+            load_v(v0, q + 2 * W);
+            update2(v1, sa, sb, kB, kB, false);
+        }
+        if (nk - k == 2) {
+            f32x4 sa, sb;
+            scores(sa, sb);
+            load_k(q + W);
+            load_v(v1, q + W);
+            update2(v0, sa, sb, kB, kB, false);
+            last_step(v1, q + W);
+        } else {
+            last_step(v0, q);
+        }
     }
 
-    float lt = l + shfl_xor(l, 16);
-    lt += shfl_xor(lt, 32);
+    if constexpr (W > 1) {
+        // Combine the W running states of the unit in wave 0 (same lane layout
+        // in every wave): M = max m_w, weights exp2(m_w - M).
+        __shared__ float sh_o[W - 1][NVT * 4][64];
+        __shared__ float sh_m[W - 1][64];
+        __shared__ float sh_l[W - 1][64];
+        if (wv > 0) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sh_o[wv - 1][4 * t + e][lane] = o[t][e];
+            sh_m[wv - 1][lane] = m;
+            sh_l[wv - 1][lane] = l;
+        }
+        __syncthreads();
+        if (wv > 0) return;
+#pragma unroll
+        for (int w = 0; w < W - 1; ++w) {
+            const float m2 = sh_m[w][lane];
+            const float mn = fmaxf(m, m2);  // finite: wave 0 always has pair 0
+            const float ca = fast_exp2(m - mn), cb = fast_exp2(m2 - mn);
+            l = l * ca + sh_l[w][lane] * cb;
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[t][e] = o[t][e] * ca + sh_o[w][4 * t + e][lane] * cb;
+            m = mn;
+        }
+    }
+
+    const float lt = xor32_sum(xor16_sum(l));
     if (t0 == 0 && t1 == ctx) {
         if (!head_ok) return;
         const float inv = 1.f / lt;
@@ -346,12 +450,15 @@ void decode_valu_kernel(const DecodeArgs a) {
     const int n = lane & 15;
     const int j = lane >> 4;
 
+    // Unit order (partition, sequence, query head), head fastest (see the MFMA
+    // kernel).  With a multiple of 8 heads, head h of every sequence runs on
+    // XCD h % 8, so sequences that share prefix blocks share that XCD's L2.
     int u = xcd_unit(blockIdx.x, a.run);
     if (u >= a.num_units) return;
-    const int s = u % a.S;
-    u /= a.S;
     const int h = u % a.Hq;
-    const int p = u / a.Hq;
+    u /= a.Hq;
+    const int s = u % a.S;
+    const int p = u / a.S;
     const int g = h / a.G;
 
     const int t0 = p * a.P;
@@ -533,7 +640,16 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
     if (grid > 0) {
         if constexpr (DT != kF32) {
             if (kind == DecodeKernel::kMfma) {
-                decode_mfma_kernel<DT, D><<<dim3(grid), dim3(64), 0, stream>>>(a);
+                switch (a.waves_per_unit) {
+                case 4:
+                    decode_mfma_kernel<DT, D, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
+                    break;
+                case 2:
+                    decode_mfma_kernel<DT, D, 2><<<dim3(grid), dim3(128), 0, stream>>>(a);
+                    break;
+                default:
+                    decode_mfma_kernel<DT, D, 1><<<dim3(grid), dim3(64), 0, stream>>>(a);
+                }
             } else {
                 decode_valu_kernel<DT, D><<<dim3(grid), dim3(64), 0, stream>>>(a);
             }

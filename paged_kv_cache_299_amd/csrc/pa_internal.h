@@ -21,6 +21,7 @@ struct DecodeArgs {
     int64_t NB;
     int num_units;          // logical work units of the launch
     int run;                // XCD run length (see xcd_unit)
+    int waves_per_unit;     // MFMA kernel: waves sharing one unit (1, 2 or 4)
 };
 
 enum class DecodeKernel { kValu, kMfma };
