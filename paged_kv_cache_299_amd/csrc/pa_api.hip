@@ -86,21 +86,21 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
 constexpr int kBlock = 16;
 constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
 constexpr int kMaxPartitions = 1 << 16;
+constexpr int64_t kTargetUnits = 2048;  // two one-wave units on each of the 1024 SIMDs
 
-// Partition length when the caller leaves it to the library.  A grouped-query
-// unit (one kv head, G query heads on MFMA) streams its tiles fastest in long
-// runs, so take the longest of 1024 / 512 tokens that still gives at least
-// four units per compute unit when every sequence is as long as the table
-// allows (the host cannot see the real lengths); one-head units on VALU do
-// more work per byte and prefer 256-token runs.
-int auto_partition(bool mfma, int64_t pairs, int max_tokens) {
-    constexpr int64_t kMinUnits = 4 * 256;
-    if (mfma) {
-        for (int P : {1024, 512}) {
-            if (pairs * (((int64_t)max_tokens + P - 1) / P) >= kMinUnits) return P;
-        }
-    }
-    return 256;
+// Partition length when the caller leaves it to the library.  Both kernels
+// run one wave per unit with one block requested ahead, and a decode step
+// streams fastest when the units fill every SIMD about twice (a compute unit
+// then has ~40 KiB of reads outstanding, where MI355X streams best; fewer
+// units leave bandwidth unused, more only queue).  The host cannot see the
+// real lengths and plans for full tables: P is the power of two in [256,
+// 1024] that gives about kTargetUnits units, or one partition per sequence
+// when that is shorter.  `rows` = sequences x (kv heads on MFMA, query heads
+// on VALU).
+int auto_partition(int64_t rows, int max_tokens) {
+    int P = 256;
+    while (P < kMaxPartition && rows * (((int64_t)max_tokens + P - 1) / P) > kTargetUnits) P *= 2;
+    return P;
 }
 
 int64_t num_partitions(int max_tokens, int P) {
@@ -210,8 +210,8 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % kBlock != 0 ||
                                                           partition_tokens > kMaxPartition)))
         return fail(PA_ERR_INVALID_ARG,
-                    "pa_decode: partition_tokens %d must be 0 or a multiple of 16 in [16, 1024]",
-                    partition_tokens);
+                    "pa_decode: partition_tokens %d must be 0 or a multiple of 16 in [16, %d]",
+                    partition_tokens, kMaxPartition);
     if (block_size != kBlock)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (only 16 is built)",
                     block_size);
@@ -233,7 +233,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
 
     int P = partition_tokens > 0
                 ? partition_tokens
-                : auto_partition(mfma, (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
+                : auto_partition((int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
                                  max_tokens);
     int64_t NP = 1;
     if (P < max_tokens) {
@@ -258,6 +258,8 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     a.ctx = context_lens;
     a.out = out;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2_abs = fabsf(scale) * 1.4426950408889634f;
+    a.q_xor = scale < 0.f ? (int)0x80008000u : 0;
     a.S = num_seqs;
     a.Hq = num_heads;
     a.Hkv = num_kv_heads;
@@ -267,8 +269,6 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     a.P = P;
     a.NB = num_blocks;
     a.num_units = (int)units;
-    a.run = 1;
-    a.waves_per_unit = 1;
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);

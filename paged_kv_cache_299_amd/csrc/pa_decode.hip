@@ -8,7 +8,7 @@
 // [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム: block
 //  table and decode equation; "online softmax (FlashAttention style)"]
 //
-// Work unit = (partition p of P tokens, kv head or query head, sequence), one
+// Work unit = (sequence, partition p of P tokens, kv head or query head), one
 // wave64 per unit.  A sequence longer than P is cut into partitions; each
 // writes (m, l, unnormalised o) and merge_kernel recombines the partitions with
 // log-sum-exp weights -- the streaming softmax is associative, so the split
@@ -18,21 +18,16 @@
 // Two partition kernels:
 //  * decode_mfma_kernel (bf16/fp16, 2..16 query heads per kv head): the G
 //    query heads of one kv head form a small dense contraction.  Per block of
-//    16 tokens: S^T[16 tok x 16 heads] = K[16 x D] . Q^T on
-//    v_mfma_f32_16x16x32 (heads padded to 16); per pair of blocks:
-//    O^T[D x 16] += V^T[D x 32 tok] . P^T, again on v_mfma_f32_16x16x32, with
-//    P split into a high and a low 16-bit part so the weights keep ~16
-//    significant bits.
+//    16 tokens: S^T[16 tok x 16 cols] = K[16 x D] . Q^T on v_mfma_f32_16x16x32
+//    and O^T[D x 16 cols] += V^T[D x 16 tok] . P^T on v_mfma_f32_16x16x16
+//    (heads padded to 16 columns), with the weights split into a high and a
+//    low 16-bit part so they keep ~16 significant bits.
 //  * decode_valu_kernel (one query head per unit; fp32, or G == 1): dot
 //    products with v_dot2 / FMA on 16-byte loads, cross-lane reductions, and
 //    P.V with the 16 weights broadcast through SGPRs.
 // Both read each (block, kv head) tile of K and of V exactly once per unit,
-// as 16-byte (K) and 8/16-byte (V) loads that cover the tile in order.  One
-// register set holds a block: the next block's K is requested as soon as the
-// scores have consumed K, its V as soon as P.V has consumed V, so every wave
-// keeps about one block in flight, and the register budget allows three (MFMA
-// kernel) or four (VALU kernel) waves per SIMD, so that all units of a decode
-// step are resident at once.
+// as 16-byte (K) and 8/16-byte (V) loads that cover the tile in order, and
+// keep one block requested ahead of the one being reduced.
 #include <math.h>
 
 #include "pa_device.h"
@@ -96,19 +91,93 @@ __device__ __forceinline__ void issue_point() {
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
 // ---------------------------------------------------------------------------
+// Work units in launch order.  Unit = (sequence s, partition p, head group g),
+// sequence-major, g fastest; a sequence has max(1, ceil(ctx / P)) partitions
+// (an empty context still gets one unit, which writes zeros).  Workgroup b
+// takes the b-th unit of this list, so the units that exist fill the front of
+// the grid and the workgroups past the end (the host sizes the grid for full
+// tables) exit at once: with all units resident, every compute unit then holds
+// the same number of units (a grid with holes left some compute units with
+// more streaming waves than others, and the decode step ran at the pace of the
+// busiest ones).  Consecutive units have consecutive g, so the 8 XCDs
+// (workgroup b runs on XCD b % 8) each take every 8th head of every partition.
+// Returns false past the last unit; otherwise s and the unit's rank r within
+// its sequence (p = r / groups, g = r % groups).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool find_unit(int b, const int *ctx, int S, int cap, int P, int groups,
+                                          int &s_out, int &r_out) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        const int s = c0 + lane;
+        int u = 0;
+        if (s < S) {
+            const int c = clamp_ctx(ctx[s], cap);
+            u = groups * (c > P ? (c + P - 1) / P : 1);
+        }
+        // inclusive prefix sum over the wave
+        int incl = u;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        // (readlane: results the compiler knows to be wave-uniform, so that
+        // addresses derived from them stay scalar)
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (b < base + total) {
+            const uint64_t past = __ballot(base + incl > b);  // lanes whose units end after b
+            const int first = __builtin_amdgcn_readfirstlane(__builtin_ctzll(past));
+            s_out = c0 + first;
+            r_out = b - (base + __builtin_amdgcn_readlane(incl - u, first));
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------------------
 // GQA partition kernel on MFMA.
 //
-// Lane l = 16 j + n.  In the QK product lane l supplies K[token n][8 dims of
-// run 4c + j] (one 16-byte load of the [D/8][16][8] K tile: instruction c of
-// the wave reads bytes [1024 c, 1024 c + 1024) of the tile) and
-// Q^T[same dims][head n]; it gets back the scores of tokens 4j..4j+3 for
-// query head n of the group.  Those four scores are exactly the B operand it
-// supplies to the P.V product, whose A operand is V^T[dim 16t + n][tokens
-// 4j..4j+3] (8 bytes of the [D][16] V tile), and whose result O^T[dims 16t +
-// 4j..4j+3][head n] stays in the lane across blocks.
+// Lane l = 16 j + n.  Column n of every product is query head n of the group
+// (heads padded to 16 with q = 0).  Per block of 16 tokens:
+//  * S^T[16 tok x 16 col] = K[16 x D] . Q^T on v_mfma_f32_16x16x32: lane l
+//    supplies K[token n][8 dims of run 4c + j] (instruction c of the wave
+//    reads bytes [1024 c, 1024 c + 1024) of the [D/8][16][8] K tile) and
+//    Q^T[same dims][col n], and gets back the scores of tokens 4j..4j+3 of
+//    column n;
+//  * O^T[D x 16 col] += V^T[D x 16 tok] . P^T on v_mfma_f32_16x16x16: lane l
+//    supplies V^T[dim 16t + n][tokens 4j..4j+3] (8 bytes of the [D][16] V
+//    tile) and exactly the four weights it computed, and O^T[dims 16t +
+//    4j..4j+3][col n] stays in the lane across blocks.
+// The weights enter the product as two 16-bit parts, hi = RNE(p) and lo =
+// RNE(p - hi), so they keep ~16 significant bits.  When 2G <= 16 both parts
+// ride in one product: columns G..2G-1 carry the same heads as columns 0..G-1
+// (same q, so the same scores and weights) and take the lo parts; the two
+// column halves are added once at the end.  Otherwise hi and lo take one
+// product each.
+//
+// One wave per unit, one block of K and V (8 KiB) requested ahead: the next
+// block is requested as soon as the scores of the current one are in.  On
+// MI355X a compute unit streams best with ~40 KiB of reads outstanding (more
+// only queues and slows the step), which the usual decode grid of ~1000-1500
+// units gives at one block per wave.  Loads go through one buffer descriptor
+// per tile whose range is empty past the unit's last block, so the request
+// needs no branch and the one past the end makes no memory traffic.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 8)))
+template <int DT> __device__ __forceinline__ f32x4 mfma16(const i32x2 &a, const i32x2 &b, const f32x4 &c) {
+    if constexpr (DT == kBF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+}
+
+template <int DT, int D, bool SPLIT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
@@ -116,33 +185,29 @@ void decode_mfma_kernel(const DecodeArgs a) {
     constexpr int NVT = D / 16;       // P.V output tiles, 16 dims each
     constexpr int TILE = D * kB * 2;  // bytes of one (block, kv head) tile
 
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;  // wave of the unit: it takes block pairs wv, wv + W, ...
+    const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
+    const int cap = a.MB * kB;
 
-    // Unit order (partition, sequence, kv head), head fastest: workgroup b runs
-    // on XCD b % 8, so with a multiple of 8 kv heads every XCD gets one head of
-    // every (sequence, partition) and the same share of work whatever the
-    // context lengths (sequence-fastest order tied each XCD to fixed sequences).
-    int u = xcd_unit(blockIdx.x, a.run);
-    if (u >= a.num_units) return;
-    const int g = u % a.Hkv;
-    u /= a.Hkv;
-    const int s = u % a.S;
-    const int p = u / a.S;
-
+    int s, r;
+    if (!find_unit(blockIdx.x, a.ctx, a.S, cap, a.P, a.Hkv, s, r)) return;
+    const int g = r % a.Hkv;
+    const int p = r / a.Hkv;
     const int t0 = p * a.P;
     const int blk0 = t0 / kB;
-    // The table slice of this partition does not depend on the context length:
-    // request it together with ctx (one round trip instead of two).
     int my_bt = blk0 + lane < a.MB ? a.bt[(int64_t)s * a.MB + blk0 + lane] : 0;
-    const int ctx = clamp_ctx(a.ctx[s], a.MB * kB);
-    const bool head_ok = n < a.G;
-    const int h = g * a.G + (head_ok ? n : 0);
+    const int ctx = clamp_ctx(a.ctx[s], cap);
+
+    // column n -> query head of the group; in SPLIT mode columns G..2G-1
+    // repeat heads 0..G-1 (they take the lo parts of the weights)
+    const bool hi_col = n < a.G;
+    const bool col_ok = SPLIT ? n < 2 * a.G : hi_col;
+    const int hn = hi_col ? n : (col_ok ? n - a.G : 0);
+    const int h = g * a.G + hn;
     uint16_t *outp = (uint16_t *)a.out + ((int64_t)s * a.Hq + h) * D;
-    if (t0 >= ctx) {
-        if (p == 0 && head_ok) {  // empty context: the output is zero
+    if (ctx == 0) {  // empty context (its only unit): the output is zero
+        if (hi_col) {
 #pragma unroll
             for (int t = 0; t < NVT; ++t) *(i32x2 *)(outp + 16 * t + 4 * j) = i32x2{0, 0};
         }
@@ -158,91 +223,58 @@ void decode_mfma_kernel(const DecodeArgs a) {
     i32x4 qf[NKC];
 #pragma unroll
     for (int c = 0; c < NKC; ++c)
-        qf[c] = head_ok ? ld16(qrow + (4 * c + j) * 8) : i32x4{0, 0, 0, 0};
+        qf[c] = col_ok ? ld16(qrow + (4 * c + j) * 8) ^ a.q_xor : i32x4{0, 0, 0, 0};
+    const float cs = a.scale_log2_abs;  // the sign of the scale went into q
 
     const char *kbase = (const char *)a.k + (int64_t)g * TILE;
     const char *vbase = (const char *)a.v + (int64_t)g * TILE;
     const int64_t blk_stride = (int64_t)a.Hkv * TILE;
 
-    float m = -INFINITY;
-    float l = 0.f;
+    float m = -INFINITY;  // reference maximum of the column, log2 units
+    float l = 0.f;        // this lane's share of the softmax denominator
     f32x4 o[NVT];
 #pragma unroll
     for (int t = 0; t < NVT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // K operand slices of a pair of blocks, and V operand slices of a pair.
-    struct KRegs {
-        i32x4 a[NKC], b[NKC];
+    struct Blk {
+        i32x4 k[NKC];
+        i32x2 v[NVT];
     };
-    struct VRegs {
-        i32x2 a[NVT], b[NVT];
-    };
-    KRegs kr;
-    VRegs v0, v1;
-
-    // Valid tokens of block b of the unit (16 except in its last block).
-    auto valid = [&](int b) {
-        const int v = t1 - (t0 + b * kB);
-        return v < 0 ? 0 : (v > kB ? kB : v);
-    };
-    // Second block of pair q; an absent one (odd block count) re-reads the
-    // first block's tile and is masked out, so every pair issues the same loads.
-    auto second = [&](int q) { return min(2 * q + 1, nblk - 1); };
-
-    auto load_k = [&](int q) {
-        const char *ka = kbase + (int64_t)__builtin_amdgcn_readlane(my_bt, 2 * q) * blk_stride;
-        const char *kb = kbase + (int64_t)__builtin_amdgcn_readlane(my_bt, second(q)) * blk_stride;
+    Blk b0, b1;
+    auto load = [&](Blk &x, int i) {
+        const bool in = i < nblk;
+        const int phys = __builtin_amdgcn_readlane(my_bt, in ? i : 0);
+        const int64_t off = (int64_t)phys * blk_stride;
+        const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+        const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) kr.a[c] = ld16_stream(ka + (64 * c + lane) * 16);
+        for (int c = 0; c < NKC; ++c) x.k[c] = bload16_stream(rk, (64 * c + lane) * 16);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) kr.b[c] = ld16_stream(kb + (64 * c + lane) * 16);
+        for (int t = 0; t < NVT; ++t) x.v[t] = bload8_stream(rv, ((16 * t + n) * kB + 4 * j) * 2);
         issue_point();
     };
-    auto load_v = [&](VRegs &r, int q) {
-        const char *va = vbase + (int64_t)__builtin_amdgcn_readlane(my_bt, 2 * q) * blk_stride;
-        const char *vb = vbase + (int64_t)__builtin_amdgcn_readlane(my_bt, second(q)) * blk_stride;
+
+    // One online-softmax step over block i (held in x); the next block goes
+    // into y.  Only the unit's last block can hold empty slots; there they are
+    // masked (score -inf, weight 0, V zeroed since it may hold NaN) in a
+    // branch of its own.  The reference maximum m moves only when the block
+    // maximum exceeds it by more than 8 (a factor 2^8): weights exp2(s - m)
+    // then stay <= 256 and the rescale of O and l is skipped for most blocks.
+    auto step = [&](Blk &x, Blk &y, int i) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) r.a[t] = ld8_stream(va + ((16 * t + n) * kB + 4 * j) * 2);
+        for (int c = 0; c < NKC; ++c) sc = mfma32<DT>(x.k[c], qf[c], sc);
+        load(y, i + 1);
+        const bool tail = i == nblk - 1;
+        int nv = kB;
+        if (tail) {
+            nv = t1 - (t0 + i * kB);
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) r.b[t] = ld8_stream(vb + ((16 * t + n) * kB + 4 * j) * 2);
-        issue_point();
-    };
-    // Scores of both blocks of the pair in kr.
-    auto scores = [&](f32x4 &sa, f32x4 &sb) {
-        sa = f32x4{0.f, 0.f, 0.f, 0.f};
-        sb = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NKC; ++c) {
-            sa = mfma32<DT>(kr.a[c], qf[c], sa);
-            sb = mfma32<DT>(kr.b[c], qf[c], sb);
+            for (int e = 0; e < 4; ++e)
+                if (4 * j + e >= nv) sc[e] = -INFINITY;
         }
-    };
-    // Mask of the 16-bit V elements of tokens 4j..4j+3 that are valid (< nv).
-    auto vmask = [&](int nv, uint32_t &m0, uint32_t &m1) {
-        m0 = (4 * j + 0 < nv ? 0x0000ffffu : 0u) | (4 * j + 1 < nv ? 0xffff0000u : 0u);
-        m1 = (4 * j + 2 < nv ? 0x0000ffffu : 0u) | (4 * j + 3 < nv ? 0xffff0000u : 0u);
-    };
-    // One online-softmax step over a pair of blocks A (nva valid tokens) and B
-    // (nvb valid).  P.V runs on v_mfma_f32_16x16x32: lane group j supplies the
-    // k-slots 8j..8j+7 = tokens 4j..4j+3 of A, then of B, which is both how its
-    // two 8-byte V slices concatenate and how its two sets of four scores do.
-    // Empty slots (only in the unit's last pair) are masked: score -inf, V
-    // zeroed (they may hold NaN).
-    //
-    // The reference maximum m moves only when a lane's block maximum exceeds it
-    // by more than 8 (a factor 2^8): weights exp2(s - m) then stay <= 256, and
-    // the rescale of O and l by exp2(m_old - m_new) is skipped for most steps.
-    auto update2 = [&](const VRegs &V, const f32x4 &sa, const f32x4 &sb, int nva, int nvb,
-                       bool mask) {
-        float sv[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = (!mask || 4 * j + e < nva) ? sa[e] * a.scale_log2 : -INFINITY;
-            sv[4 + e] = (!mask || 4 * j + e < nvb) ? sb[e] * a.scale_log2 : -INFINITY;
-        }
-        float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        bm = xor32_max(xor16_max(bm));
+        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        bm = xor32_max(xor16_max(bm)) * cs;  // the block has a valid token
         const bool grow = bm > m + 8.f;
         if (__any(grow)) {
             const float mn = grow ? bm : m;
@@ -252,124 +284,71 @@ void decode_mfma_kernel(const DecodeArgs a) {
             l *= alpha;
             m = mn;
         }
-        float pe[8];
+        const float nm = -m;
+        float pe[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(sv[e] - m);
-        l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-        // P = hi + lo, both 16-bit: hi = RNE(p), lo = RNE(p - hi).
-        uint32_t hb[8], lb[8];
+        for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(fmaf(sc[e], cs, nm));
+        if (tail) {  // (-inf) * 0 is NaN when the scale is 0
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            hb[e] = to_bits16<DT>(pe[e]);
-            lb[e] = to_bits16<DT>(pe[e] - from_bits16<DT>(hb[e]));
-        }
-        const i32x4 phi = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16)),
-                           (int)(hb[4] | (hb[5] << 16)), (int)(hb[6] | (hb[7] << 16))};
-        const i32x4 plo = {(int)(lb[0] | (lb[1] << 16)), (int)(lb[2] | (lb[3] << 16)),
-                           (int)(lb[4] | (lb[5] << 16)), (int)(lb[6] | (lb[7] << 16))};
-        uint32_t ma0 = 0xffffffffu, ma1 = 0xffffffffu, mb0 = 0xffffffffu, mb1 = 0xffffffffu;
-        if (mask) {
-            vmask(nva, ma0, ma1);
-            vmask(nvb, mb0, mb1);
-        }
+            for (int e = 0; e < 4; ++e)
+                if (4 * j + e >= nv) pe[e] = 0.f;
+            const uint32_t m0 = (4 * j + 0 < nv ? 0x0000ffffu : 0u) | (4 * j + 1 < nv ? 0xffff0000u : 0u);
+            const uint32_t m1 = (4 * j + 2 < nv ? 0x0000ffffu : 0u) | (4 * j + 3 < nv ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) {
-            const i32x4 vv = {(int)((uint32_t)V.a[t][0] & ma0), (int)((uint32_t)V.a[t][1] & ma1),
-                              (int)((uint32_t)V.b[t][0] & mb0), (int)((uint32_t)V.b[t][1] & mb1)};
-            o[t] = mfma32<DT>(vv, phi, o[t]);
-            o[t] = mfma32<DT>(vv, plo, o[t]);
+            for (int t = 0; t < NVT; ++t)
+                x.v[t] = i32x2{(int)((uint32_t)x.v[t][0] & m0), (int)((uint32_t)x.v[t][1] & m1)};
         }
-    };
-    auto last_step = [&](const VRegs &V, int q) {
-        f32x4 sa, sb;
-        scores(sa, sb);
-        update2(V, sa, sb, valid(2 * q), 2 * q + 1 < nblk ? valid(2 * q + 1) : 0, true);
-    };
-
-    // Pairs of this wave: q = wv, wv + W, ...  One K register set and two V
-    // sets: right after the scores of pair q consume K, both K and V of the
-    // wave's next pair are requested (V into the other set), so a whole pair
-    // is in flight while pair q is reduced.  The loop is unrolled by two so the
-    // V sets alternate without copies, and issues its loads without conditions
-    // so the wait counts stay exact; the wave's last pair is masked.
-    const int npairs = (nblk + 1) / 2;
-    const int nk = npairs > wv ? (npairs - wv + W - 1) / W : 0;  // pairs of this wave
-    if (nk > 0) {
-        int q = wv;
-        int k = 0;
-        load_k(q);
-        load_v(v0, q);
-        for (; k + 2 < nk; k += 2, q += 2 * W) {  // pairs q, q + W full; q + 2W exists
-            f32x4 sa, sb;
-            scores(sa, sb);
-            load_k(q + W);
-            load_v(v1, q + W);
-            update2(v0, sa, sb, kB, kB, false);
-            scores(sa, sb);
-            load_k(q + 2 * W);
-            load_v(v0, q + 2 * W);
-            update2(v1, sa, sb, kB, kB, false);
-        }
-        if (nk - k == 2) {
-            f32x4 sa, sb;
-            scores(sa, sb);
-            load_k(q + W);
-            load_v(v1, q + W);
-            update2(v0, sa, sb, kB, kB, false);
-            last_step(v1, q + W);
+        l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        // P = hi + lo, both 16-bit: hi = RNE(p), lo = RNE(p - hi) (p - hi is exact)
+        const uint32_t h0 = pack2<DT>(pe[0], pe[1]);
+        const uint32_t h1 = pack2<DT>(pe[2], pe[3]);
+        const uint32_t l0 = pack2<DT>(pe[0] - elem_lo<DT>(h0), pe[1] - elem_hi<DT>(h0));
+        const uint32_t l1 = pack2<DT>(pe[2] - elem_lo<DT>(h1), pe[3] - elem_hi<DT>(h1));
+        if constexpr (SPLIT) {
+            const i32x2 pw = hi_col ? i32x2{(int)h0, (int)h1} : i32x2{(int)l0, (int)l1};
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) o[t] = mfma16<DT>(x.v[t], pw, o[t]);
         } else {
-            last_step(v0, q);
+            const i32x2 phi = {(int)h0, (int)h1}, plo = {(int)l0, (int)l1};
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+                o[t] = mfma16<DT>(x.v[t], phi, o[t]);
+                o[t] = mfma16<DT>(x.v[t], plo, o[t]);
+            }
         }
-    }
+    };
 
-    if constexpr (W > 1) {
-        // Combine the W running states of the unit in wave 0 (same lane layout
-        // in every wave): M = max m_w, weights exp2(m_w - M).
-        __shared__ float sh_o[W - 1][NVT * 4][64];
-        __shared__ float sh_m[W - 1][64];
-        __shared__ float sh_l[W - 1][64];
-        if (wv > 0) {
-#pragma unroll
-            for (int t = 0; t < NVT; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sh_o[wv - 1][4 * t + e][lane] = o[t][e];
-            sh_m[wv - 1][lane] = m;
-            sh_l[wv - 1][lane] = l;
-        }
-        __syncthreads();
-        if (wv > 0) return;
-#pragma unroll
-        for (int w = 0; w < W - 1; ++w) {
-            const float m2 = sh_m[w][lane];
-            const float mn = fmaxf(m, m2);  // finite: wave 0 always has pair 0
-            const float ca = fast_exp2(m - mn), cb = fast_exp2(m2 - mn);
-            l = l * ca + sh_l[w][lane] * cb;
-#pragma unroll
-            for (int t = 0; t < NVT; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[t][e] = o[t][e] * ca + sh_o[w][4 * t + e][lane] * cb;
-            m = mn;
-        }
+    // One exit, at the loop test (an exit between the two steps would give the
+    // loop head a second predecessor with another load order, and the wait
+    // counts there would have to cover both).
+    load(b0, 0);
+    int i = 0;
+    for (; i + 2 <= nblk; i += 2) {
+        step(b0, b1, i);
+        step(b1, b0, i + 1);
     }
+    if (i < nblk) step(b0, b1, i);
 
-    const float lt = xor32_sum(xor16_sum(l));
-    if (t0 == 0 && t1 == ctx) {
-        if (!head_ok) return;
+    if constexpr (SPLIT) {
+        // add the lo columns G..2G-1 into the hi columns 0..G-1
+#pragma unroll
+        for (int t = 0; t < NVT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[t][e] += __shfl_down(o[t][e], a.G, 16);
+    }
+    const float lt = xor32_sum(xor16_sum(l));  // all lanes take part in the swaps
+    if (!hi_col) return;
+    if (t0 == 0 && t1 == ctx) {  // the unit covers the whole context
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < NVT; ++t) store4<DT>(outp + 16 * t + 4 * j, o[t], inv);
         return;
     }
     const int64_t part = ((int64_t)s * a.Hq + h) * a.NP + p;
-    if (head_ok) {
-        float *po = a.part_o + part * D;
+    float *po = a.part_o + part * D;
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
-        if (j == 0) {
-            a.part_ml[2 * part] = m;
-            a.part_ml[2 * part + 1] = lt;
-        }
-    }
+    for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
+    if (j == 0) *(float2 *)(a.part_ml + 2 * part) = float2{m, lt};
 }
 
 // ---------------------------------------------------------------------------
@@ -434,8 +413,10 @@ template <int DT> __device__ __forceinline__ float v_elem(const i32x4 *w, int t)
     }
 }
 
+// fp32 rows at D = 128 need more registers than four waves per SIMD allow
 template <int DT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(DT == kF32 && D == 128 ? 3 : 4, 8)))
 void decode_valu_kernel(const DecodeArgs a) {
     constexpr int E = Elem<DT>::bytes;
     constexpr int X = 16 / E;     // elements per 16-byte run
@@ -450,15 +431,12 @@ void decode_valu_kernel(const DecodeArgs a) {
     const int n = lane & 15;
     const int j = lane >> 4;
 
-    // Unit order (partition, sequence, query head), head fastest (see the MFMA
-    // kernel).  With a multiple of 8 heads, head h of every sequence runs on
-    // XCD h % 8, so sequences that share prefix blocks share that XCD's L2.
-    int u = xcd_unit(blockIdx.x, a.run);
-    if (u >= a.num_units) return;
-    const int h = u % a.Hq;
-    u /= a.Hq;
-    const int s = u % a.S;
-    const int p = u / a.S;
+    // Units in the order of find_unit (sequence-major, head fastest).  With a
+    // multiple of 8 heads, head h of a sequence runs on XCD (offset + h) % 8.
+    int s, r;
+    if (!find_unit(blockIdx.x, a.ctx, a.S, a.MB * kB, a.P, a.Hq, s, r)) return;
+    const int h = r % a.Hq;
+    const int p = r / a.Hq;
     const int g = h / a.G;
 
     const int t0 = p * a.P;
@@ -573,83 +551,79 @@ void decode_valu_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one (sequence, query head).
-// 256 threads = PG partition lanes x D/4 four-dim groups.  Each thread merges
-// partitions pg, pg + PG, ... of its four dims with a running log-sum-exp
-//   M' = max(M, m_q),  L' = L e^(M-M') + l_q e^(m_q-M'),  o' likewise,
-// so the loads of all its partitions are independent and go out together;
-// the PG running states are then combined the same way through LDS.
+// Log-sum-exp merge of the partitions of one (sequence, query head), one wave
+// per row, lane l owning dims [D/64 l, D/64 (l + 1)):
+//   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise.
+// The partition count follows from the context length; the results of the
+// first kSpec partitions are requested together with it (all NP partition
+// slots exist in the workspace, stale ones are never combined), so merging up
+// to kSpec partitions costs one round trip.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
-    constexpr int E = Elem<DT>::bytes;
-    constexpr int DQ = D / 4;        // four-dim groups
-    constexpr int PG = 256 / DQ;     // partition lanes
-    const int tid = threadIdx.x;
-    const int dq = tid % DQ;
-    const int pg = tid / DQ;
-    const int sh = blockIdx.x;       // s * Hq + h
-    const int s = sh / a.Hq;
+    constexpr int DL = D / 64;  // dims per lane
+    constexpr int kSpec = 8;
+    static_assert(DL == 1 || DL == 2, "head_dim 64 or 128");
+    typedef float fv __attribute__((ext_vector_type(DL)));
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hq + h
+    if (row >= a.S * a.Hq) return;
+    const int s = row / a.Hq;
+    const float *pml = a.part_ml + (int64_t)row * a.NP * 2;
+    const float *po = a.part_o + (int64_t)row * a.NP * D + DL * lane;
+    float2 ml[kSpec];
+    fv ov[kSpec];
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q) {
+        if (q < a.NP) {
+            ml[q] = *(const float2 *)(pml + 2 * q);
+            ov[q] = *(const fv *)(po + (int64_t)q * D);
+        }
+    }
     const int ctx = clamp_ctx(a.ctx[s], a.MB * kB);
-    const int np = (ctx + a.P - 1) / a.P;
+    const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
     if (np <= 1) return;  // written by the partition kernel
-
-    __shared__ f32x4 o_sh[PG][DQ];
-    __shared__ float m_sh[PG][DQ];
-    __shared__ float l_sh[PG][DQ];
-
-    const float *pml = a.part_ml + (int64_t)sh * a.NP * 2;
-    const float *po = a.part_o + (int64_t)sh * a.NP * D + dq * 4;
     float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int q = pg; q < np; q += PG) {
-        const float mq = pml[2 * q];
-        const float lq = pml[2 * q + 1];
-        const f32x4 oq = *(const f32x4 *)(po + (int64_t)q * D);
-        const float Mn = fmaxf(M, mq);
+    fv acc = {};
+    auto add = [&](float mq, float lq, const fv &oq) {
+        const float Mn = fmaxf(M, mq);  // m_q is finite: every partition has a token
         const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
         L = L * ca + lq * cb;
         acc = acc * ca + oq * cb;
         M = Mn;
-    }
-    o_sh[pg][dq] = acc;
-    m_sh[pg][dq] = M;
-    l_sh[pg][dq] = L;
-    __syncthreads();
-    if (pg == 0) {
-        float Mt = m_sh[0][dq];
-        for (int r = 1; r < PG; ++r) Mt = fmaxf(Mt, m_sh[r][dq]);
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-        float lsum = 0.f;
-        for (int r = 0; r < PG; ++r) {
-            // a lane that got no partition holds M = -inf, L = 0, o = 0
-            const float w = fast_exp2(m_sh[r][dq] - Mt);
-            lsum += l_sh[r][dq] * w;
-            sum += o_sh[r][dq] * w;
+    };
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q)
+        if (q < np) add(ml[q].x, ml[q].y, ov[q]);
+#pragma unroll 4
+    for (int q = kSpec; q < np; ++q)
+        add(pml[2 * q], pml[2 * q + 1], *(const fv *)(po + (int64_t)q * D));
+    const float inv = 1.f / L;
+    char *dst = (char *)a.out + ((int64_t)row * D + DL * lane) * Elem<DT>::bytes;
+    if constexpr (DL == 2) {
+        if constexpr (DT == kF32) {
+            *(float2 *)dst = float2{acc[0] * inv, acc[1] * inv};
+        } else {
+            *(uint32_t *)dst = pack2<DT>(acc[0] * inv, acc[1] * inv);
         }
-        store4<DT>((char *)a.out + ((int64_t)sh * D + dq * 4) * E, sum, 1.f / lsum);
+    } else {
+        store1<DT>(dst, acc[0] * inv);
     }
 }
 
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream_t stream) {
-    const int per = 8 * a.run;
-    const int grid = (a.num_units + per - 1) / per * per;
+    // one workgroup per possible unit (the host plans for full tables); the
+    // ones past the real units exit at once
+    const int grid = a.num_units;
     if (grid > 0) {
         if constexpr (DT != kF32) {
             if (kind == DecodeKernel::kMfma) {
-                switch (a.waves_per_unit) {
-                case 4:
-                    decode_mfma_kernel<DT, D, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
-                    break;
-                case 2:
-                    decode_mfma_kernel<DT, D, 2><<<dim3(grid), dim3(128), 0, stream>>>(a);
-                    break;
-                default:
-                    decode_mfma_kernel<DT, D, 1><<<dim3(grid), dim3(64), 0, stream>>>(a);
-                }
+                if (2 * a.G <= 16)
+                    decode_mfma_kernel<DT, D, true><<<dim3(grid), dim3(64), 0, stream>>>(a);
+                else
+                    decode_mfma_kernel<DT, D, false><<<dim3(grid), dim3(64), 0, stream>>>(a);
             } else {
                 decode_valu_kernel<DT, D><<<dim3(grid), dim3(64), 0, stream>>>(a);
             }
@@ -660,7 +634,8 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
         if (e != hipSuccess) return e;
     }
     if (a.NP > 1 && a.S > 0) {
-        merge_kernel<DT, D><<<dim3(a.S * a.Hq), dim3(256), 0, stream>>>(a);
+        const int rows = a.S * a.Hq;
+        merge_kernel<DT, D><<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(a);
         return hipGetLastError();
     }
     return hipSuccess;

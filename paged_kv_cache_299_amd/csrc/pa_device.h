@@ -12,6 +12,7 @@ enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -110,14 +111,35 @@ __device__ __forceinline__ i32x2 ld8_stream(const void *p) {
     return __builtin_nontemporal_load((const i32x2 *)p);
 }
 
-// Workgroups go to the 8 XCDs round-robin (workgroup b runs on XCD b % 8).
-// Map workgroup b to logical unit u so that every XCD takes runs of `run`
-// consecutive units: XCD x gets [r*8*run + x*run, r*8*run + (x+1)*run) for
-// r = 0, 1, ...  Units next to each other in logical order then share an L2.
-__device__ __forceinline__ int xcd_unit(int b, int run) {
-    const int x = b & 7;
-    const int k = b >> 3;
-    return (k / run) * 8 * run + x * run + (k % run);
+// Two fp32 values -> one word of two 16-bit values (round to nearest even),
+// the first in the low half: one v_cvt_pk_* on gfx950.
+template <int DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (DT == kBF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+    }
+}
+
+// ---- buffer loads ------------------------------------------------------------
+// Loads through a buffer descriptor check every lane's offset against the
+// descriptor's byte range: a lane outside it reads zeros and makes no memory
+// request.  A descriptor over one K or V tile (range = tile bytes, or 0 for a
+// block that does not exist) lets a kernel issue the loads of a block ahead
+// without a branch: past the end they cost nothing and return zeros.
+// Word 3 is the gfx9-family value: 32-bit data format (untyped loads need a
+// non-zero format), no swizzle, no index stride.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;  // nontemporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ i32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
+}
+__device__ __forceinline__ i32x2 bload8_stream(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyNT));
 }
 
 }  // namespace pa

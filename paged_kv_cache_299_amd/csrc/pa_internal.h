@@ -17,11 +17,11 @@ struct DecodeArgs {
     float *part_o;          // [S][Hq][NP][D]   (split path only)
     float *part_ml;         // [S][Hq][NP][2]   (m in log2 units, l)
     float scale_log2;       // scale * log2(e)
+    float scale_log2_abs;   // |scale| * log2(e)
+    int q_xor;              // 0x80008000 when scale < 0: flips the sign of 16-bit q
     int S, Hq, Hkv, G, MB, NP, P;
     int64_t NB;
-    int num_units;          // logical work units of the launch
-    int run;                // XCD run length (see xcd_unit)
-    int waves_per_unit;     // MFMA kernel: waves sharing one unit (1, 2 or 4)
+    int num_units;          // workgroups of the launch: an upper bound on the units
 };
 
 enum class DecodeKernel { kValu, kMfma };
