@@ -10,13 +10,18 @@ independent KV pools (one per model layer, all sharing the block tables, as
 a real decode iteration does), so no step finds its K/V in the caches of the
 previous one.
 
+Steps are launched as HIP graph replays, one captured graph per pass over the
+layers: an eager launch from Python costs about as much host time as the GPU
+work, and every graph launch adds a few microseconds of GPU idle time.
+
 Prints ONE JSON line.  `value` = algorithmic bytes of the step / step time
 (GB/s, decimal), tokens/s = sequences / step time.  `roofline` covers
-pa_decode (its partition kernel plus the merge kernel, timed with HIP events
-on the launch stream).  `cpu_baseline` times the CPU oracle on the same
+pa_decode (its partition kernel plus the merge kernel), timed with HIP events
+on the launch stream over graph replays of the decode alone.  `cpu_baseline` times the CPU oracle on the same
 inputs (layer 0) on this host's cores.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -82,6 +87,27 @@ def raw_bits(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def measured_traffic(workload, part, root=ROOT):
+    """HBM bytes per pa_decode launch from the committed counter summary
+    (profiles/decode_<workload>_traffic.json: rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes scaled by a plain copy's), or None when no summary exists
+    for this workload and partitioning or the kernel sources have changed since
+    the counters were taken (the summary records their SHA-256)."""
+    rel = os.path.join("profiles", f"decode_{workload}_traffic.json")
+    path = os.path.join(root, rel)
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload or rec.get("partition_tokens") != (part or "auto"):
+        return None, rel
+    for src, digest in rec["sources_sha256"].items():
+        with open(os.path.join(root, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None, rel
+    return int(rec["bytes_per_launch"]), rel
 
 
 def decode_bytes(ctx, S, Hq, Hkv, D, B, e):
@@ -155,46 +181,80 @@ def main():
             T = st.slot_mapping.shape[0]
             step_bytes += 2 * 2 * T * Hkv * D * e + 8 * T
 
-    def run_step(i, evs=None):
-        k, v = pools[i % len(pools)]
-        if evs is not None:
-            evs[0].record()
-        for st in steps:
-            if st[0] == "copy":
-                pa.pa_copy_blocks(k, v, st[1])
-            else:
-                pa.pa_write_kv(st[1], st[2], k, v, st[3])
-        if evs is not None:
-            evs[1].record()
-        pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part)
-        if evs is not None:
-            evs[2].record()
+    L = len(pools)
+    stream = torch.cuda.Stream()  # default priority
 
-    for i in range(args.warmup):
-        run_step(i)
+    def enqueue(layer, write=True, decode=True):
+        k, v = pools[layer]
+        if write:
+            for st in steps:
+                if st[0] == "copy":
+                    pa.pa_copy_blocks(k, v, st[1])
+                else:
+                    pa.pa_write_kv(st[1], st[2], k, v, st[3])
+        if decode:
+            pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part)
+
+    # eager warmup on the capture stream (grows the library's workspace for it)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            enqueue(i % L)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # HIP graphs: launching a decode step from Python (ctypes marshalling of
+    # two calls) takes about as long as the GPU work, and each graph launch
+    # leaves the GPU idle for several microseconds, so one graph holds a whole
+    # pass over the layers -- as a model's decode iteration would be captured.
+    # Replays are idempotent: the writes store the same tokens in the same slots.
+    def capture(layers, **phase):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for l in layers:
+                enqueue(l, **phase)
+        return g
+
+    def timed(n, **phase):
+        """Runs exactly n steps of the phase (layer i % L for step i) as graph
+        replays; wall seconds and GPU ms (HIP events on the launch stream)."""
+        q_, r_ = divmod(n, L)
+        g_all = capture(range(L), **phase)
+        g_rest = capture(range(r_), **phase) if r_ else None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g_all.replay()  # warm
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(q_):
+                g_all.replay()
+            if g_rest is not None:
+                g_rest.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1)
+
+    # timed region: exactly `steps` steps
+    wall, _ = timed(args.steps)
     ms_per_step = wall * 1e3 / args.steps
-    decode_ms = [a[1].elapsed_time(a[2]) for a in evs]
-    write_ms = [a[0].elapsed_time(a[1]) for a in evs]
-    dec_avg = statistics.fmean(decode_ms)
+    # the kernels alone, per launch: pa_decode (partition + merge kernels) and
+    # the KV writes (plus block copies for copy-on-write)
+    _, dec_ms = timed(args.steps, write=False)
+    _, wr_ms = timed(args.steps, decode=False)
+    dec_avg = dec_ms / args.steps
+    wr_avg = wr_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
+    traffic, traffic_src = measured_traffic(args.workload, part)
 
     # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
     cpu = None
     if args.cpu_reps > 0:
         import oracle
         k0, v0 = pools[0]
-        run_step(0)
+        with torch.cuda.stream(stream):
+            enqueue(0)
         torch.cuda.synchronize()
         kh, vh = raw_bits(k0.cpu()), raw_bits(v0.cpu())
         code = pa.DTYPE_CODES[dt]
@@ -235,10 +295,12 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),
         "decode_us": round(dec_avg * 1e3, 2),
-        "write_us": round(statistics.fmean(write_ms) * 1e3, 2),
+        "write_us": round(wr_avg * 1e3, 2),
+        "launch": "HIP graph replays, one graph per pass over the rotated layers",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "kernel": "pa_decode (partition + merge kernels)",
+                     "traffic": traffic, "traffic_source": traffic_src,
+                     "kernel": "pa_decode (partition + merge kernels)",
                      "bytes_per_launch": int(dec_bytes)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

@@ -96,9 +96,12 @@ int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cac
  *
  * Long contexts are split into partitions whose partial results are merged
  * with log-sum-exp weights; the library keeps a grow-only workspace for them
- * per (device, stream) (PA_ERR_NO_MEMORY if it cannot be allocated).  Results
- * are bit-identical from run to run and do not depend on where the physical
- * blocks sit.
+ * per (device, stream) (PA_ERR_NO_MEMORY if it cannot be allocated).  A
+ * workspace buffer is never freed before pa_release_workspaces, so a HIP graph
+ * that captured pa_decode stays valid; the first call on a stream that needs
+ * a larger workspace allocates one (hipMalloc), so make that call before
+ * capturing.  Results are bit-identical from run to run and do not depend on
+ * where the physical blocks sit.
  * Supports block_size 16, head_dim 64 or 128, num_heads a multiple of
  * num_kv_heads; PA_ERR_UNSUPPORTED otherwise.
  */
@@ -153,8 +156,10 @@ const char *pa_last_error(void);
 int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,
                                   int max_blocks_per_seq, int partition_tokens);
 
-/* Frees the library-owned decode workspaces after synchronising the device.
- * Call only when no pa_decode work is pending on any stream. */
+/* Frees the library-owned decode workspaces (including buffers that larger
+ * ones replaced) after synchronising each device that holds one.  Call only
+ * when no pa_decode work is pending and no captured graph that uses them will
+ * be replayed again. */
 int pa_release_workspaces(void);
 
 /* Library ABI version (major * 10000 + minor * 100 + patch). */

@@ -12,6 +12,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
@@ -47,9 +48,13 @@ int elem_bytes(int dtype) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- split workspace: one grow-only buffer per (device, stream) ------------
+// A buffer that a larger one replaces is kept, not freed, until
+// pa_release_workspaces: work already queued on the stream, and HIP graphs that
+// captured a launch, keep using the buffer they were given.
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void *> retired;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -61,22 +66,17 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[{dev, stream}];
     if (w.bytes < need) {
-        if (w.ptr) {
-            // the old buffer may still be in use by work queued on this stream
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        const size_t bytes = need < (size_t)(1 << 20) ? (size_t)(1 << 20) : need;
-        e = hipMalloc(&w.ptr, bytes);
+        size_t bytes = need < (size_t)(1 << 20) ? (size_t)(1 << 20) : need;
+        if (bytes < 2 * w.bytes) bytes = 2 * w.bytes;  // geometric growth
+        void *p = nullptr;
+        e = hipMalloc(&p, bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            w.ptr = nullptr;
             return fail(PA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes,
                         hipGetErrorString(e));
         }
+        if (w.ptr) w.retired.push_back(w.ptr);
+        w.ptr = p;
         w.bytes = bytes;
     }
     *out = w.ptr;
@@ -86,21 +86,23 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
 constexpr int kBlock = 16;
 constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
 constexpr int kMaxPartitions = 1 << 16;
-constexpr int64_t kTargetUnits = 2048;  // two one-wave units on each of the 1024 SIMDs
 
-// Partition length when the caller leaves it to the library.  Both kernels
-// run one wave per unit with one block requested ahead, and a decode step
-// streams fastest when the units fill every SIMD about twice (a compute unit
-// then has ~40 KiB of reads outstanding, where MI355X streams best; fewer
-// units leave bandwidth unused, more only queue).  The host cannot see the
-// real lengths and plans for full tables: P is the power of two in [256,
-// 1024] that gives about kTargetUnits units, or one partition per sequence
-// when that is shorter.  `rows` = sequences x (kv heads on MFMA, query heads
-// on VALU).
-int auto_partition(int64_t rows, int max_tokens) {
-    int P = 256;
-    while (P < kMaxPartition && rows * (((int64_t)max_tokens + P - 1) / P) > kTargetUnits) P *= 2;
-    return P;
+// Partition length when the caller leaves it to the library: the longest P
+// (up to `longest`) whose units, counted for full tables (the host cannot
+// see the real lengths), still number at least `min_units`; else 256.  Both
+// kernels run one wave per unit with one block requested ahead, and a decode
+// step streams fastest with about 40 KiB of reads outstanding per compute
+// unit: fewer, longer units cut the partials the merge reads, too few units
+// leave bandwidth unused.  Measured on MI355X:
+// the GQA kernel (rows = sequences x kv heads) is fastest at P = 1024 with
+// >= 1024 units, the one-head VALU kernel (rows = sequences x query heads,
+// more arithmetic per byte) at P = 512 with >= 2048 units.
+int auto_partition(bool mfma, int64_t rows, int max_tokens) {
+    const int longest = mfma ? 1024 : 512;
+    const int64_t min_units = mfma ? 1024 : 2048;
+    for (int P = longest; P > 256; P /= 2)
+        if (rows * (((int64_t)max_tokens + P - 1) / P) >= min_units) return P;
+    return 256;
 }
 
 int64_t num_partitions(int max_tokens, int P) {
@@ -233,7 +235,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
 
     int P = partition_tokens > 0
                 ? partition_tokens
-                : auto_partition((int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
+                : auto_partition(mfma, (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
                                  max_tokens);
     int64_t NP = 1;
     if (P < max_tokens) {
@@ -297,18 +299,25 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
 int pa_release_workspaces(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     int rc = PA_OK;
-    for (auto &kv : g_ws) {
-        if (!kv.second.ptr) continue;
-        int prev = 0;
-        (void)hipGetDevice(&prev);
-        (void)hipSetDevice(kv.first.first);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    for (auto it = g_ws.begin(); it != g_ws.end();) {
+        Workspace &w = it->second;
+        (void)hipSetDevice(it->first.first);
         hipError_t e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipFree(kv.second.ptr);
-        if (e != hipSuccess) rc = hip_fail(e, "pa_release_workspaces");
-        (void)hipSetDevice(prev);
-        kv.second = Workspace{};
+        if (e != hipSuccess) {  // keep the buffers: work may still use them
+            rc = hip_fail(e, "pa_release_workspaces");
+            ++it;
+            continue;
+        }
+        if (w.ptr) w.retired.push_back(w.ptr);
+        for (void *p : w.retired) {
+            e = hipFree(p);
+            if (e != hipSuccess) rc = hip_fail(e, "pa_release_workspaces");
+        }
+        it = g_ws.erase(it);
     }
-    g_ws.clear();
+    (void)hipSetDevice(prev);
     return rc;
 }
 

@@ -551,41 +551,43 @@ void decode_valu_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one (sequence, query head), one wave
-// per row, lane l owning dims [D/64 l, D/64 (l + 1)):
+// Log-sum-exp merge of the partitions of one (sequence, query head) by D/4
+// lanes, four dims each:
 //   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise.
 // The partition count follows from the context length; the results of the
 // first kSpec partitions are requested together with it (all NP partition
 // slots exist in the workspace, stale ones are never combined), so merging up
 // to kSpec partitions costs one round trip.
 // ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
-    constexpr int DL = D / 64;  // dims per lane
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a) {
+    constexpr int LPR = D / 4;                // lanes per row
+    constexpr int RPB = kMergeThreads / LPR;  // rows per workgroup
     constexpr int kSpec = 8;
-    static_assert(DL == 1 || DL == 2, "head_dim 64 or 128");
-    typedef float fv __attribute__((ext_vector_type(DL)));
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hq + h
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x * RPB + tid / LPR;  // s * Hq + h
+    const int d0 = (tid % LPR) * 4;
     if (row >= a.S * a.Hq) return;
     const int s = row / a.Hq;
     const float *pml = a.part_ml + (int64_t)row * a.NP * 2;
-    const float *po = a.part_o + (int64_t)row * a.NP * D + DL * lane;
+    const float *po = a.part_o + (int64_t)row * a.NP * D + d0;
     float2 ml[kSpec];
-    fv ov[kSpec];
+    f32x4 ov[kSpec];
 #pragma unroll
     for (int q = 0; q < kSpec; ++q) {
         if (q < a.NP) {
             ml[q] = *(const float2 *)(pml + 2 * q);
-            ov[q] = *(const fv *)(po + (int64_t)q * D);
+            ov[q] = *(const f32x4 *)(po + (int64_t)q * D);
         }
     }
     const int ctx = clamp_ctx(a.ctx[s], a.MB * kB);
     const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
     if (np <= 1) return;  // written by the partition kernel
     float M = -INFINITY, L = 0.f;
-    fv acc = {};
-    auto add = [&](float mq, float lq, const fv &oq) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](float mq, float lq, const f32x4 &oq) {
         const float Mn = fmaxf(M, mq);  // m_q is finite: every partition has a token
         const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
         L = L * ca + lq * cb;
@@ -597,18 +599,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
         if (q < np) add(ml[q].x, ml[q].y, ov[q]);
 #pragma unroll 4
     for (int q = kSpec; q < np; ++q)
-        add(pml[2 * q], pml[2 * q + 1], *(const fv *)(po + (int64_t)q * D));
-    const float inv = 1.f / L;
-    char *dst = (char *)a.out + ((int64_t)row * D + DL * lane) * Elem<DT>::bytes;
-    if constexpr (DL == 2) {
-        if constexpr (DT == kF32) {
-            *(float2 *)dst = float2{acc[0] * inv, acc[1] * inv};
-        } else {
-            *(uint32_t *)dst = pack2<DT>(acc[0] * inv, acc[1] * inv);
-        }
-    } else {
-        store1<DT>(dst, acc[0] * inv);
-    }
+        add(pml[2 * q], pml[2 * q + 1], *(const f32x4 *)(po + (int64_t)q * D));
+    store4<DT>((char *)a.out + ((int64_t)row * D + d0) * Elem<DT>::bytes, acc, 1.f / L);
 }
 
 // ---------------------------------------------------------------------------
@@ -634,8 +626,10 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
         if (e != hipSuccess) return e;
     }
     if (a.NP > 1 && a.S > 0) {
+        const int rows_per_block = kMergeThreads / (D / 4);
         const int rows = a.S * a.Hq;
-        merge_kernel<DT, D><<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(a);
+        merge_kernel<DT, D><<<dim3((rows + rows_per_block - 1) / rows_per_block),
+                               dim3(kMergeThreads), 0, stream>>>(a);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -166,3 +166,65 @@ def test_workload_full_size(dev, name):
     run_full_case(case, dev, partition_tokens=P, strict=True)
     if P:
         run_full_case(case, dev, partition_tokens=0, strict=True)
+
+
+# --------------------------------------------------------------------------
+# unit search over many sequences (the kernels find their unit from the
+# context lengths 64 sequences at a time), the sign of the scale, and replays
+# of a captured HIP graph
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(8, 2, torch.bfloat16), (4, 4, torch.float16)])
+def test_many_sequences_with_empty_ones(dev, Hq, Hkv, dtype):
+    log(f"200 sequences Hq={Hq} Hkv={Hkv} {dtype}")
+    rng = np.random.default_rng(11)
+    ctx = rng.integers(0, 300, size=200)
+    ctx[rng.choice(200, size=30, replace=False)] = 0
+    ctx[[0, 63, 64, 127, 128, 199]] = [0, 257, 1, 0, 300, 16]
+    case = _case([int(c) for c in ctx], Hq, Hkv, 64, dtype, seed=12, MB=20)
+    for P in (0, 64, 128):
+        g, _, _ = run_full_case(case, dev, partition_tokens=P, strict=False)
+        out = g.out.cpu()
+        zero = case.context_lens == 0
+        assert (out[zero] == 0).all()
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8)])
+def test_negative_and_zero_scale(dev, scale, Hq, Hkv):
+    log(f"scale {scale} Hq={Hq} Hkv={Hkv}")
+    case = _case([1, 17, 300, 700], Hq, Hkv, 128, torch.bfloat16, seed=13)
+    case.scale = scale
+    for P in (0, 256):
+        run_full_case(case, dev, partition_tokens=P, strict=False)
+
+
+def test_graph_replay_matches_eager(dev):
+    log("graph capture of write + decode, replayed")
+    case = _case([300, 47, 1024, 1, 0, 700], 32, 8, 128, torch.bfloat16, seed=14)
+    g = GpuCase(case, dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g.apply_steps()
+        eager = g.decode(256).clone()  # also grows the workspace of this stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        g.apply_steps()
+        pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, g.out, partition_tokens=256)
+    kc, vc = oracle_apply_steps(case)
+    ref = oracle_decode(case, kc, vc)
+    for rep in range(3):
+        with torch.cuda.stream(stream):
+            g.out.zero_()
+            graph.replay()
+        torch.cuda.synchronize()
+        got = g.out.cpu()
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        # eager work on the same pools and output between replays; on the
+        # capture stream, a split finer than the captured one makes the library
+        # grow that stream's workspace, which must not disturb the graph
+        other = g.decode(0)
+        check_decode(other, ref, case.dtype, f"eager after replay {rep}", strict=False)
+        with torch.cuda.stream(stream):
+            finer = g.decode(16 if rep == 0 else 32)
+        check_decode(finer, ref, case.dtype, f"finer split after replay {rep}", strict=False)

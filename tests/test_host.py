@@ -141,3 +141,22 @@ def test_workload_draws_are_seeded_and_in_range():
     assert torch.equal(c1.q, c2.q) and torch.equal(c1.block_tables, c2.block_tables)
     assert torch.equal(c1.k_cache.isnan(), c2.k_cache.isnan())
     assert c1.block_tables[0, 1:].tolist() == [-1, -1]
+
+
+def test_bench_traffic_record_is_used_only_for_the_recorded_kernel(tmp_path):
+    """bench.py reports the committed HBM-traffic figure only for the workload,
+    partitioning and kernel sources the counters were taken with."""
+    import hashlib
+    import json
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    (tmp_path / "profiles").mkdir()
+    rec = {"workload": "llama3_8b", "partition_tokens": "auto", "bytes_per_launch": 1234,
+           "sources_sha256": {"k.hip": hashlib.sha256(b"kernel v1").hexdigest()}}
+    (tmp_path / "profiles" / "decode_llama3_8b_traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("llama3_8b", 0, root=str(tmp_path))[0] == 1234
+    assert bench.measured_traffic("llama3_8b", 512, root=str(tmp_path))[0] is None
+    assert bench.measured_traffic("opt_13b", 0, root=str(tmp_path)) == (None, None)
+    src.write_text("kernel v2")
+    assert bench.measured_traffic("llama3_8b", 0, root=str(tmp_path))[0] is None
