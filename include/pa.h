@@ -113,10 +113,13 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
 /*
  * pa_decode_ex -- pa_decode with an explicit partition length.
  *   partition_tokens  0 = choose automatically (what pa_decode does);
- *                     otherwise a multiple of 16 in [16, 1024]: every
- *                     sequence is cut into runs of that many tokens, each run
- *                     is reduced on its own and the runs are merged.  A value
- *                     >= max_blocks_per_seq * B gives the single-pass kernel.
+ *                     otherwise a multiple of 16 in [16, 1024]: a sequence
+ *                     of ctx tokens is cut into the fewest runs of at most
+ *                     that many tokens, ceil(ctx / partition_tokens), all of
+ *                     the same number of whole blocks but a shorter last one;
+ *                     each run is reduced on its own and the runs are merged.
+ *                     A value >= max_blocks_per_seq * B gives the single-pass
+ *                     kernel.
  * The split is exact up to rounding: the streaming softmax is associative.
  *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
  *    online softmax ("FlashAttention style")]

@@ -8,8 +8,9 @@
 // [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム: block
 //  table and decode equation; "online softmax (FlashAttention style)"]
 //
-// Work unit = (sequence, partition p of P tokens, kv head or query head), one
-// wave64 per unit.  A sequence longer than P is cut into partitions; each
+// Work unit = (sequence, partition p, kv head or query head), one wave64 per
+// unit.  A sequence longer than P tokens is cut into the fewest partitions of
+// at most P tokens, equal in whole blocks (blocks_per_partition); each
 // writes (m, l, unnormalised o) and merge_kernel recombines the partitions with
 // log-sum-exp weights -- the streaming softmax is associative, so the split
 // only changes rounding.  A sequence that fits one partition is normalised and
@@ -91,6 +92,22 @@ __device__ __forceinline__ void issue_point() {
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
 // ---------------------------------------------------------------------------
+// A context of ctx tokens is cut into the fewest partitions of at most P
+// tokens, ceil(ctx / P), all of the same number of whole blocks except a
+// shorter last one (a 1100-token context at P = 1024 gives 2 x 35 blocks, not
+// 64 + 5): the partitions of a sequence then take about the same time, and
+// fewer units run at the full length P.  Returns the blocks per partition;
+// every partition holds at least one token (ceil(nb / ceil(nb / n)) = n for
+// n = ceil(nb / PB), the partition count the units are counted with).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int blocks_per_partition(int ctx, int P) {
+    const int nb = (ctx + kB - 1) / kB;
+    if (ctx <= P) return nb;
+    const int n = (ctx + P - 1) / P;
+    return (nb + n - 1) / n;
+}
+
+// ---------------------------------------------------------------------------
 // Work units in launch order.  Unit = (sequence s, partition p, head group g),
 // sequence-major, g fastest; a sequence has max(1, ceil(ctx / P)) partitions
 // (an empty context still gets one unit, which writes zeros).  Workgroup b
@@ -101,20 +118,18 @@ __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c
 // more streaming waves than others, and the decode step ran at the pace of the
 // busiest ones).  Consecutive units have consecutive g, so the 8 XCDs
 // (workgroup b runs on XCD b % 8) each take every 8th head of every partition.
-// Returns false past the last unit; otherwise s and the unit's rank r within
-// its sequence (p = r / groups, g = r % groups).
+// Returns false past the last unit; otherwise s, its clamped context length
+// and the unit's rank r within its sequence (p = r / groups, g = r % groups).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool find_unit(int b, const int *ctx, int S, int cap, int P, int groups,
-                                          int &s_out, int &r_out) {
+                                          int &s_out, int &ctx_out, int &r_out) {
     const int lane = threadIdx.x & 63;
     int base = 0;
     for (int c0 = 0; c0 < S; c0 += 64) {
         const int s = c0 + lane;
         int u = 0;
-        if (s < S) {
-            const int c = clamp_ctx(ctx[s], cap);
-            u = groups * (c > P ? (c + P - 1) / P : 1);
-        }
+        const int c = s < S ? clamp_ctx(ctx[s], cap) : 0;
+        if (s < S) u = groups * (c > P ? (c + P - 1) / P : 1);
         // inclusive prefix sum over the wave
         int incl = u;
 #pragma unroll
@@ -129,6 +144,7 @@ __device__ __forceinline__ bool find_unit(int b, const int *ctx, int S, int cap,
             const uint64_t past = __ballot(base + incl > b);  // lanes whose units end after b
             const int first = __builtin_amdgcn_readfirstlane(__builtin_ctzll(past));
             s_out = c0 + first;
+            ctx_out = __builtin_amdgcn_readlane(c, first);
             r_out = b - (base + __builtin_amdgcn_readlane(incl - u, first));
             return true;
         }
@@ -190,14 +206,14 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int j = lane >> 4;
     const int cap = a.MB * kB;
 
-    int s, r;
-    if (!find_unit(blockIdx.x, a.ctx, a.S, cap, a.P, a.Hkv, s, r)) return;
+    int s, ctx, r;
+    if (!find_unit(blockIdx.x, a.ctx, a.S, cap, a.P, a.Hkv, s, ctx, r)) return;
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
-    const int t0 = p * a.P;
-    const int blk0 = t0 / kB;
+    const int per = blocks_per_partition(ctx, a.P);
+    const int blk0 = p * per;
+    const int t0 = blk0 * kB;
     int my_bt = blk0 + lane < a.MB ? a.bt[(int64_t)s * a.MB + blk0 + lane] : 0;
-    const int ctx = clamp_ctx(a.ctx[s], cap);
 
     // column n -> query head of the group; in SPLIT mode columns G..2G-1
     // repeat heads 0..G-1 (they take the lo parts of the weights)
@@ -213,7 +229,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
         }
         return;
     }
-    const int t1 = min(ctx, t0 + a.P);
+    const int t1 = min(ctx, t0 + per * kB);
     const int nblk = (t1 - t0 + kB - 1) / kB;  // 1..64
     // entries past the context are never used; out-of-range ids are clamped so
     // that no read leaves the pool
@@ -433,16 +449,16 @@ void decode_valu_kernel(const DecodeArgs a) {
 
     // Units in the order of find_unit (sequence-major, head fastest).  With a
     // multiple of 8 heads, head h of a sequence runs on XCD (offset + h) % 8.
-    int s, r;
-    if (!find_unit(blockIdx.x, a.ctx, a.S, a.MB * kB, a.P, a.Hq, s, r)) return;
+    int s, ctx, r;
+    if (!find_unit(blockIdx.x, a.ctx, a.S, a.MB * kB, a.P, a.Hq, s, ctx, r)) return;
     const int h = r % a.Hq;
     const int p = r / a.Hq;
     const int g = h / a.G;
 
-    const int t0 = p * a.P;
-    const int blk0 = t0 / kB;
+    const int per = blocks_per_partition(ctx, a.P);
+    const int blk0 = p * per;
+    const int t0 = blk0 * kB;
     int my_bt = blk0 + lane < a.MB ? a.bt[(int64_t)s * a.MB + blk0 + lane] : 0;
-    const int ctx = clamp_ctx(a.ctx[s], a.MB * kB);
     char *outp = (char *)a.out + ((int64_t)s * a.Hq + h) * D * E;
     if (t0 >= ctx) {
         if (p == 0) {
@@ -451,7 +467,7 @@ void decode_valu_kernel(const DecodeArgs a) {
         }
         return;
     }
-    const int t1 = min(ctx, t0 + a.P);
+    const int t1 = min(ctx, t0 + per * kB);
     const int nblk = (t1 - t0 + kB - 1) / kB;
     if (lane >= nblk || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
 
