@@ -146,6 +146,10 @@ int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cac
         return fail(PA_ERR_INVALID_ARG, "pa_write_kv: head_dim %d must be a multiple of %d, <= 512",
                     head_dim, x);
     if (num_tokens == 0) return PA_OK;
+    const int64_t tile_tokens = 256 / (head_dim / x);  // tokens per workgroup
+    if ((num_tokens + tile_tokens - 1) / tile_tokens * num_kv_heads > 0x7fffffff)
+        return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: %lld tokens x %d kv heads in one call",
+                    (long long)num_tokens, num_kv_heads);
     if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
         return fail(PA_ERR_INVALID_ARG, "pa_write_kv: null pointer");
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||

@@ -139,6 +139,36 @@ def test_write_kv_bit_exact_with_skips(dev, dtype):
     assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_write_kv_runs_of_consecutive_slots(dev, dtype):
+    """Runs of consecutive aligned slots (stored as 16-byte V runs) mixed with
+    misaligned runs, skips inside a run and a partial trailing group."""
+    log(f"write_kv runs {dtype}")
+    case = _case([40, 3, 160], 8, 4, 128, dtype, seed=15, NB=64)
+    B = 16
+    runs = [
+        np.arange(5 * B, 6 * B),            # one whole block
+        np.arange(7 * B + 8, 8 * B),        # second half of a block
+        np.arange(9 * B + 4, 9 * B + 12),   # 8 slots starting at offset 4
+        np.arange(10 * B, 10 * B + 8),      # first half, then a skip inside the next run
+        np.array([11 * B, 11 * B + 1, -1, 11 * B + 3, 11 * B + 4, 11 * B + 5, 11 * B + 6,
+                  11 * B + 7]),
+        np.arange(12 * B + 8, 12 * B + 8 + 24),  # crosses into the next block
+        np.arange(20 * B, 20 * B + 5),      # partial trailing group
+    ]
+    slots = np.concatenate(runs).astype(np.int64)
+    T = slots.shape[0]
+    rng = np.random.default_rng(16)
+    kn = torch.from_numpy(rng.standard_normal((T, 4, 128)).astype(np.float32)).to(dtype)
+    vn = torch.from_numpy(rng.standard_normal((T, 4, 128)).astype(np.float32)).to(dtype)
+    case.steps = [workloads.WriteStep(kn, vn, torch.from_numpy(slots))]
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    torch.cuda.synchronize()
+    kc, vc = oracle_apply_steps(case)
+    assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc)
+
+
 def test_copy_blocks_bit_exact(dev):
     log("copy_blocks")
     case = _case([40, 3, 160], 32, 32, 128, torch.bfloat16, seed=8, NB=200)
