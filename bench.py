@@ -172,6 +172,8 @@ def main():
     setup_s = time.time() - t_setup
 
     ctx = case.context_lens.tolist()
+    # the hint a serving system gives from its block reference counts
+    shared = workloads.shares_blocks(case.block_tables, case.context_lens, B)
     dec_bytes = decode_bytes(ctx, S, Hq, Hkv, D, B, e)
     step_bytes = dec_bytes
     for st in case.steps:
@@ -193,7 +195,8 @@ def main():
                 else:
                     pa.pa_write_kv(st[1], st[2], k, v, st[3])
         if decode:
-            pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part)
+            pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part,
+                         shared_blocks=shared)
 
     # eager warmup on the capture stream (grows the library's workspace for it)
     with torch.cuda.stream(stream):
@@ -290,7 +293,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
                    "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
-                   "partition_tokens": part or "auto", "layers_rotated": args.layers},
+                   "partition_tokens": part or "auto", "shared_blocks_hint": shared,
+                   "layers_rotated": args.layers},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),

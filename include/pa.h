@@ -110,8 +110,19 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
 
+/* Flags of pa_decode_ex. */
+enum pa_decode_flags {
+    /* Hint: physical blocks of this call are read by several sequences
+     * (shared prompt prefixes, parallel sampling; reference count > 1).  K/V
+     * are then read with cacheable loads so that the sequences sharing a
+     * block hit in L2; without the hint they are streamed with nontemporal
+     * loads, which is faster when every block is read once.  Results are
+     * bit-identical either way. */
+    PA_DECODE_SHARED_BLOCKS = 1
+};
+
 /*
- * pa_decode_ex -- pa_decode with an explicit partition length.
+ * pa_decode_ex -- pa_decode with an explicit partition length and flags.
  *   partition_tokens  0 = choose automatically (what pa_decode does);
  *                     otherwise a multiple of 16 in [16, 1024]: a sequence
  *                     of ctx tokens is cut into the fewest runs of at most
@@ -120,6 +131,8 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
  *                     each run is reduced on its own and the runs are merged.
  *                     A value >= max_blocks_per_seq * B gives the single-pass
  *                     kernel.
+ *   flags             0 or PA_DECODE_SHARED_BLOCKS (a hint, see above);
+ *                     other bits give PA_ERR_INVALID_ARG.
  * The split is exact up to rounding: the streaming softmax is associative.
  *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
  *    online softmax ("FlashAttention style")]
@@ -128,7 +141,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *block_tables, const int32_t *context_lens, float scale,
                  void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                  int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
-                 int partition_tokens, void *stream);
+                 int partition_tokens, int flags, void *stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks, the copy step of

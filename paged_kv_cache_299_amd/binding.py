@@ -8,7 +8,8 @@ no fallback.  If libpa.so is missing, loading raises.
 Shapes (see layout.py for the pool format):
   pa_write_kv(k_new [T,Hkv,D], v_new [T,Hkv,D], k_cache, v_cache, slot_mapping int64 [T])
   pa_decode(q [S,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
-            scale, out [S,Hq,D], stream=None, partition_tokens=0)
+            scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
+    (calls pa_decode_ex; shared_blocks sets the PA_DECODE_SHARED_BLOCKS hint)
   pa_copy_blocks(k_cache, v_cache, block_mapping int64 [n,2])
 """
 from __future__ import annotations
@@ -26,6 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa.so")
 _lib = None
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(5)
+PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
@@ -61,7 +63,7 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I64, I32, P]
     lib.pa_decode.restype = I32
     lib.pa_decode_ex.argtypes = [P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I64, I32,
-                                 I32, P]
+                                 I32, I32, P]
     lib.pa_decode_ex.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
@@ -142,7 +144,8 @@ def pa_write_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
 
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-              out: torch.Tensor, stream=None, partition_tokens: Optional[int] = 0) -> None:
+              out: torch.Tensor, stream=None, partition_tokens: Optional[int] = 0,
+              shared_blocks: bool = False) -> None:
     NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
     _need(out.shape == q.shape and out.dtype == q.dtype == k_cache.dtype,
@@ -158,6 +161,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D,
                                      B, block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
                                      int(partition_tokens or 0),
+                                     PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
 

@@ -87,17 +87,24 @@ constexpr int kBlock = 16;
 constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
 constexpr int kMaxPartitions = 1 << 16;
 
-// Partition length when the caller leaves it to the library: the longest P
-// (up to `longest`) whose units, counted for full tables (the host cannot
-// see the real lengths), still number at least `min_units`; else 256.  Both
-// kernels run one wave per unit with one block requested ahead, and a decode
-// step streams fastest with about 40 KiB of reads outstanding per compute
-// unit: fewer, longer units cut the partials the merge reads, too few units
-// leave bandwidth unused.  Measured on MI355X:
-// the GQA kernel (rows = sequences x kv heads) is fastest at P = 1024 with
-// >= 1024 units, the one-head VALU kernel (rows = sequences x query heads,
-// more arithmetic per byte) at P = 512 with >= 2048 units.
+// Partition length when the caller leaves it to the library (the host cannot
+// see the real lengths and counts units for full tables; rows = sequences x
+// kv heads on MFMA, x query heads on VALU).  Both kernels run one wave per
+// unit with one block requested ahead; a decode step streams fastest with
+// about 40 KiB of reads outstanding per compute unit and with every compute
+// unit busy to the end.  Measured on MI355X:
+//  * rows >= 2048 (e.g. 64 sequences x 40 heads): the rows alone fill the
+//    machine, and short units (P = 256) keep it evenly loaded to the end
+//    (more units than resident waves, so finished ones are replaced):
+//    OPT-13B-shaped MHA 156 us at P = 256 vs 162 us at P = 1024;
+//  * fewer rows (32 sequences x 8 kv heads): rows must be split for
+//    parallelism, and long units cut the partials the merge reads: the
+//    longest P <= 1024 with >= 1024 units (Llama-3-8B-shaped: P = 1024,
+//    53.7 us vs 54.9 at 512 and 58.1 at 256);
+//  * the VALU kernel (fp32 data or more than 16 query heads per kv head)
+//    does more arithmetic per byte and takes P <= 512 with >= 2048 units.
 int auto_partition(bool mfma, int64_t rows, int max_tokens) {
+    if (mfma && rows >= 2048) return 256;
     const int longest = mfma ? 1024 : 512;
     const int64_t min_units = mfma ? 1024 : 2048;
     for (int P = longest; P > 256; P /= 2)
@@ -203,7 +210,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *block_tables, const int32_t *context_lens, float scale,
                  void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                  int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
-                 int partition_tokens, void *stream) {
+                 int partition_tokens, int flags, void *stream) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -213,6 +220,8 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads %d is not a multiple of %d",
                     num_heads, num_kv_heads);
     if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale is not finite");
+    if (flags & ~PA_DECODE_SHARED_BLOCKS)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown flags 0x%x", flags);
     if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % kBlock != 0 ||
                                                           partition_tokens > kMaxPartition)))
         return fail(PA_ERR_INVALID_ARG,
@@ -235,7 +244,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
 
     const int G = num_heads / num_kv_heads;
     const int max_tokens = max_blocks_per_seq * kBlock;
-    const bool mfma = dtype != PA_F32 && G >= 2 && G <= 16;
+    const bool mfma = dtype != PA_F32 && G <= 16;
 
     int P = partition_tokens > 0
                 ? partition_tokens
@@ -275,6 +284,7 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     a.P = P;
     a.NB = num_blocks;
     a.num_units = (int)units;
+    a.shared_blocks = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
@@ -297,7 +307,7 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream) {
     return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
                         num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                        num_blocks, dtype, 0, stream);
+                        num_blocks, dtype, 0, 0, stream);
 }
 
 int pa_release_workspaces(void) {

@@ -17,13 +17,15 @@
 // written by its single unit directly.
 //
 // Two partition kernels:
-//  * decode_mfma_kernel (bf16/fp16, 2..16 query heads per kv head): the G
-//    query heads of one kv head form a small dense contraction.  Per block of
+//  * decode_mfma_kernel (bf16/fp16, 1..16 query heads per kv head): the G
+//    query heads of one kv head form a small dense contraction (at G = 1 the
+//    MFMA is mostly idle, but a block still costs far fewer instructions than
+//    on VALU).  Per block of
 //    16 tokens: S^T[16 tok x 16 cols] = K[16 x D] . Q^T on v_mfma_f32_16x16x32
 //    and O^T[D x 16 cols] += V^T[D x 16 tok] . P^T on v_mfma_f32_16x16x16
 //    (heads padded to 16 columns), with the weights split into a high and a
 //    low 16-bit part so they keep ~16 significant bits.
-//  * decode_valu_kernel (one query head per unit; fp32, or G == 1): dot
+//  * decode_valu_kernel (one query head per unit; fp32, or G > 16): dot
 //    products with v_dot2 / FMA on 16-byte loads, cross-lane reductions, and
 //    P.V with the 16 weights broadcast through SGPRs.
 // Both read each (block, kv head) tile of K and of V exactly once per unit,
@@ -192,7 +194,7 @@ template <int DT> __device__ __forceinline__ f32x4 mfma16(const i32x2 &a, const 
     }
 }
 
-template <int DT, int D, bool SPLIT>
+template <int DT, int D, bool SPLIT, int POLICY>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
@@ -264,9 +266,9 @@ void decode_mfma_kernel(const DecodeArgs a) {
         const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
         const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) x.k[c] = bload16_stream(rk, (64 * c + lane) * 16);
+        for (int c = 0; c < NKC; ++c) x.k[c] = bload16<POLICY>(rk, (64 * c + lane) * 16);
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) x.v[t] = bload8_stream(rv, ((16 * t + n) * kB + 4 * j) * 2);
+        for (int t = 0; t < NVT; ++t) x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * kB + 4 * j) * 2);
         issue_point();
     };
 
@@ -628,10 +630,18 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
     if (grid > 0) {
         if constexpr (DT != kF32) {
             if (kind == DecodeKernel::kMfma) {
-                if (2 * a.G <= 16)
-                    decode_mfma_kernel<DT, D, true><<<dim3(grid), dim3(64), 0, stream>>>(a);
-                else
-                    decode_mfma_kernel<DT, D, false><<<dim3(grid), dim3(64), 0, stream>>>(a);
+                const bool split = 2 * a.G <= 16;
+                if (a.shared_blocks) {
+                    if (split)
+                        decode_mfma_kernel<DT, D, true, kCachePolicyPlain><<<grid, 64, 0, stream>>>(a);
+                    else
+                        decode_mfma_kernel<DT, D, false, kCachePolicyPlain><<<grid, 64, 0, stream>>>(a);
+                } else {
+                    if (split)
+                        decode_mfma_kernel<DT, D, true, kCachePolicyNT><<<grid, 64, 0, stream>>>(a);
+                    else
+                        decode_mfma_kernel<DT, D, false, kCachePolicyNT><<<grid, 64, 0, stream>>>(a);
+                }
             } else {
                 decode_valu_kernel<DT, D><<<dim3(grid), dim3(64), 0, stream>>>(a);
             }

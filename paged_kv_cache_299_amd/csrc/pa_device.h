@@ -130,16 +130,20 @@ template <int DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi) 
 // Word 3 is the gfx9-family value: 32-bit data format (untyped loads need a
 // non-zero format), no swizzle, no index stride.
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kCachePolicyNT = 2;  // nontemporal
+// Cache policy of the K/V tile loads: nontemporal (each tile is read once per
+// decode: it should not displace reusable lines), or plain, so that several
+// sequences reading the same physical block (shared prefixes) hit in L2.
+constexpr int kCachePolicyNT = 2;
+constexpr int kCachePolicyPlain = 0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, kRsrcWord3);
 }
-__device__ __forceinline__ i32x4 bload16_stream(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
+template <int POLICY> __device__ __forceinline__ i32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
 }
-__device__ __forceinline__ i32x2 bload8_stream(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyNT));
+template <int POLICY> __device__ __forceinline__ i32x2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
 }
 
 }  // namespace pa

@@ -22,6 +22,7 @@ struct DecodeArgs {
     int S, Hq, Hkv, G, MB, NP, P;
     int64_t NB;
     int num_units;          // workgroups of the launch: an upper bound on the units
+    int shared_blocks;      // MFMA kernel: K/V with cacheable loads (blocks read by several sequences)
 };
 
 enum class DecodeKernel { kValu, kMfma };

@@ -248,6 +248,16 @@ def parallel_sampling(seed: int = 4, cow: bool = False, num_prompts: int = 16,
     return case
 
 
+def shares_blocks(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int) -> bool:
+    """True when a physical block appears in the used part of more than one
+    table row (a block with reference count > 1): the hint pa_decode_ex takes
+    as PA_DECODE_SHARED_BLOCKS."""
+    bt = block_tables.numpy()
+    used = [bt[s, :-(-int(c) // block_size)] for s, c in enumerate(context_lens.tolist())]
+    ids = np.concatenate(used) if used else np.zeros(0, dtype=bt.dtype)
+    return bool(ids.size) and np.unique(ids).size < ids.size
+
+
 CASES = {
     "tiny": tiny,
     "llama3_8b": llama3_8b,

@@ -41,12 +41,13 @@ def test_status_strings_and_version():
 
 def _decode(lib, **kw):
     args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, bt=ALIGNED, ctx=ALIGNED, scale=0.1, out=ALIGNED,
-                S=4, Hq=32, Hkv=8, D=128, B=16, MB=16, NB=100, dtype=BF16, P=0, stream=None)
+                S=4, Hq=32, Hkv=8, D=128, B=16, MB=16, NB=100, dtype=BF16, P=0, flags=0,
+                stream=None)
     args.update(kw)
     return lib.pa_decode_ex(args["q"], args["k"], args["v"], args["bt"], args["ctx"],
                             args["scale"], args["out"], args["S"], args["Hq"], args["Hkv"],
                             args["D"], args["B"], args["MB"], args["NB"], args["dtype"], args["P"],
-                            args["stream"])
+                            args["flags"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -57,6 +58,7 @@ def _decode(lib, **kw):
     (dict(scale=float("inf")), INVALID),
     (dict(P=20), INVALID),
     (dict(P=2048), INVALID),
+    (dict(flags=2), INVALID),
     (dict(B=32), UNSUPPORTED),
     (dict(D=96), UNSUPPORTED),
     (dict(q=None), INVALID),

@@ -99,6 +99,23 @@ def test_split_and_single_pass_agree_and_are_deterministic(dev):
         assert torch.equal(again.view(torch.int16), outs[P].view(torch.int16)), "not deterministic"
 
 
+def test_shared_blocks_hint_gives_identical_results(dev):
+    log("shared-blocks hint")
+    case = workloads.CASES["parallel_sampling"](num_prompts=2, samples=4, num_blocks=512,
+                                                max_private=40)
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    ref = oracle_decode(case, *oracle_apply_steps(case))
+    for P in (0, 256):
+        pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, g.out, partition_tokens=P)
+        a = g.out.cpu()
+        pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, g.out, partition_tokens=P,
+                     shared_blocks=True)
+        b = g.out.cpu()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        check_decode(b, ref, case.dtype, f"shared hint P={P}")
+
+
 def test_physical_placement_does_not_change_gpu_output(dev):
     log("placement invariance on GPU")
     for Hq, Hkv in ((32, 8), (8, 8)):

@@ -160,3 +160,15 @@ def test_bench_traffic_record_is_used_only_for_the_recorded_kernel(tmp_path):
     assert bench.measured_traffic("opt_13b", 0, root=str(tmp_path)) == (None, None)
     src.write_text("kernel v2")
     assert bench.measured_traffic("llama3_8b", 0, root=str(tmp_path))[0] is None
+
+
+def test_shares_blocks_reads_only_the_used_part_of_the_tables():
+    from paged_kv_cache_299_amd.workloads import shares_blocks
+    bt = torch.tensor([[3, 4, -1], [5, 4, 9]], dtype=torch.int32)
+    assert shares_blocks(bt, torch.tensor([32, 17], dtype=torch.int32), 16)      # block 4 twice
+    assert not shares_blocks(bt, torch.tensor([16, 17], dtype=torch.int32), 16)  # 4 unused in row 0
+    assert not shares_blocks(bt, torch.tensor([0, 0], dtype=torch.int32), 16)
+    ps = workloads.CASES["parallel_sampling"](fill=False, num_prompts=2, samples=3, num_blocks=512)
+    assert shares_blocks(ps.block_tables, ps.context_lens, 16)
+    ll = workloads.CASES["llama3_8b"](fill=False)
+    assert not shares_blocks(ll.block_tables, ll.context_lens, 16)
