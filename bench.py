@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=None,
                     help="partition tokens for pa_decode (default: the workload's, else auto)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions (0 = skip)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="draw of the workload (default: the workload's own seed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's plain copy of a 1 GiB tensor (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale)")
@@ -144,7 +146,8 @@ def main():
     torch.cuda.set_device(dev)
 
     t_setup = time.time()
-    case = workloads.CASES[args.workload](fill=False)
+    case = workloads.CASES[args.workload](
+        fill=False, **({} if args.seed is None else {"seed": args.seed}))
     S, Hq, Hkv, D, B = case.num_seqs, case.num_heads, case.num_kv_heads, case.head_dim, \
         case.block_size
     NB, dt = case.num_blocks, case.dtype
@@ -293,7 +296,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
                    "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
-                   "partition_tokens": part or "auto", "shared_blocks_hint": shared,
+                   "seed": case.seed, "partition_tokens": part or "auto",
+                   "shared_blocks_hint": shared,
                    "layers_rotated": args.layers},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
