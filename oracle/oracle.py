@@ -57,6 +57,8 @@ def _load():
     lib.oracle_write_kv.restype = I32
     lib.oracle_copy_blocks.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32]
     lib.oracle_copy_blocks.restype = I32
+    lib.oracle_swap_blocks.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32]
+    lib.oracle_swap_blocks.restype = I32
     lib.oracle_kv_cache_bytes.argtypes = [I64, I64, I64, I64, I64]
     lib.oracle_kv_cache_bytes.restype = I64
     lib.oracle_blocks_for_tokens.argtypes = [I64, I64]
@@ -178,6 +180,24 @@ def copy_blocks(k_cache, v_cache, block_mapping, *, num_kv_heads, head_dim, bloc
                                 head_dim, block_size, NB, dtype)
     _check(rc)
     return kc, vc
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, *, num_kv_heads, head_dim,
+                block_size, dtype):
+    """Copy whole blocks from the source pools into copies of the destination
+    pools (src block -> dst block per pair); returns (dst_k', dst_v')."""
+    lib = _load()
+    sk = np.ascontiguousarray(_raw(src_k, dtype))
+    sv = np.ascontiguousarray(_raw(src_v, dtype))
+    dk = _raw(dst_k, dtype).copy()
+    dv = _raw(dst_v, dtype).copy()
+    bm = np.ascontiguousarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    per = num_kv_heads * block_size * head_dim
+    rc = lib.oracle_swap_blocks(_ptr(sk), _ptr(sv), _ptr(dk), _ptr(dv), _ptr(bm), bm.shape[0],
+                                num_kv_heads, head_dim, block_size, sk.size // per, dk.size // per,
+                                dtype)
+    _check(rc)
+    return dk, dv
 
 
 def kv_cache_bytes(t, L, H, D_h, elem_bytes=2):

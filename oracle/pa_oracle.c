@@ -26,6 +26,11 @@
  *   oracle_copy_blocks        copy of whole physical blocks, the copy step of
  *                             copy-on-write.  [論文解説: PagedAttention,
  *                             技術的詳細 › Copy-on-Write KVキャッシュ共有]
+ *   oracle_swap_blocks        copy of whole blocks from one pair of pools to
+ *                             another (device pools to a host pool and back),
+ *                             the swapping the scheduler uses to preempt a
+ *                             sequence.  [論文解説: PagedAttention,
+ *                             実装のポイント › スケジューラ]
  *
  * Readings where the page is silent (each also listed in the design notes):
  *   - only tokens i < ctx contribute; the rest of the last block is ignored
@@ -353,6 +358,35 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mappin
                block_bytes);
     }
     free(snap);
+    return OR_OK;
+}
+
+/* Copy block src of the source pools to block dst of the destination pools,
+ * for every (src, dst) pair: all kv heads, all slots, K and V, byte for byte.
+ * The two pool pairs are different allocations (swap-out: device to host;
+ * swap-in: host to device), so there is no overlap to order; destinations
+ * must still be distinct (two pairs may not write one block). */
+int oracle_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                       const int64_t *block_mapping, int64_t n, int64_t Hkv, int64_t D, int64_t B,
+                       int64_t src_blocks, int64_t dst_blocks, int dtype) {
+    int64_t e = oracle_elem_bytes(dtype);
+    if (e == 0) return OR_BAD_DTYPE;
+    if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || src_blocks < 0 || dst_blocks < 0)
+        return OR_BAD_DIMS;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return OR_BAD_PAIR;
+        for (int64_t j = 0; j < i; ++j)
+            if (block_mapping[2 * j + 1] == dst) return OR_BAD_PAIR;
+    }
+    size_t block_bytes = (size_t)(Hkv * B * D * e);
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        memcpy((char *)dst_k + dst * block_bytes, (const char *)src_k + src * block_bytes,
+               block_bytes);
+        memcpy((char *)dst_v + dst * block_bytes, (const char *)src_v + src * block_bytes,
+               block_bytes);
+    }
     return OR_OK;
 }
 

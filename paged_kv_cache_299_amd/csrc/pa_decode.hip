@@ -577,7 +577,9 @@ void decode_valu_kernel(const DecodeArgs a) {
 // slots exist in the workspace, stale ones are never combined), so merging up
 // to kSpec partitions costs one round trip.
 // ---------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
+// 128 threads = 4 rows at D = 128: measured 0.7 us faster per decode step than
+// 256 (8 rows, half the compute units idle) or 64 (2 rows).
+constexpr int kMergeThreads = 128;
 
 template <int DT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a) {

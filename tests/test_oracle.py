@@ -407,3 +407,62 @@ def test_copy_blocks_rejects_overlapping_or_bad_pairs(pairs):
     with pytest.raises(OracleError):
         oracle.copy_blocks(raw(k0), raw(v0), np.array(pairs), num_kv_heads=1, head_dim=4,
                            block_size=4, dtype=F32)
+
+
+# --------------------------------------------------------------------------
+# swapping blocks out to a host pool and back (preemption by swapping)
+# --------------------------------------------------------------------------
+def test_swap_blocks_matches_numpy_indexing_and_leaves_other_blocks():
+    rng = np.random.default_rng(31)
+    NB, NH, Hkv, D, B = 9, 5, 2, 8, 4
+    k0 = rng.standard_normal((NB, Hkv, D // 4, B, 4)).astype(np.float32)
+    v0 = rng.standard_normal((NB, Hkv, D, B)).astype(np.float32)
+    hk = rng.standard_normal((NH, Hkv, D // 4, B, 4)).astype(np.float32)
+    hv = rng.standard_normal((NH, Hkv, D, B)).astype(np.float32)
+    pairs = np.array([[7, 0], [2, 4], [7, 3]], dtype=np.int64)  # one source read twice
+    gk, gv = oracle.swap_blocks(k0, v0, hk, hv, pairs, num_kv_heads=Hkv, head_dim=D,
+                                block_size=B, dtype=F32)
+    ek, ev = hk.copy(), hv.copy()
+    ek[pairs[:, 1]] = k0[pairs[:, 0]]
+    ev[pairs[:, 1]] = v0[pairs[:, 0]]
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+    assert np.array_equal(gk[[1, 2]], hk[[1, 2]])      # untouched host blocks
+    assert np.array_equal(k0, k0.copy())               # sources are read only
+
+
+@pytest.mark.parametrize("pairs", [[[1, 2], [3, 2]], [[9, 0]], [[0, 5]], [[-1, 0]]])
+def test_swap_blocks_rejects_bad_pairs(pairs):
+    k0, v0 = empty_pools(9, 1, 4, 4, torch.float32, 4, 0.0)
+    h0, hv0 = empty_pools(5, 1, 4, 4, torch.float32, 4, 0.0)
+    with pytest.raises(OracleError):
+        oracle.swap_blocks(raw(k0), raw(v0), raw(h0), raw(hv0), np.array(pairs), num_kv_heads=1,
+                           head_dim=4, block_size=4, dtype=F32)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16])
+def test_swap_out_and_in_preserves_attention(dtype):
+    """A preempted sequence's blocks go to the host pool and come back into
+    other device blocks; with the table remapped, decode gives the same
+    output bit for bit (the oracle sums in logical order)."""
+    rng = np.random.default_rng(32)
+    tdt = TORCH_DTYPE[dtype]
+    NB, NH, Hkv, Hq, D, B, ctx = 12, 6, 2, 4, 16, 4, 17
+    x = k_chunk(tdt)
+    k0 = torch.from_numpy(rng.standard_normal((NB, Hkv, D // x, B, x)).astype(np.float32)).to(tdt)
+    v0 = torch.from_numpy(rng.standard_normal((NB, Hkv, D, B)).astype(np.float32)).to(tdt)
+    q = torch.from_numpy(rng.standard_normal((1, Hq, D)).astype(np.float32)).to(tdt)
+    table = np.array([[3, 8, 1, 10, 5]], dtype=np.int32)
+    cl = np.array([ctx], dtype=np.int32)
+    kw = dict(num_kv_heads=Hkv, head_dim=D, block_size=B, k_x=x, dtype=dtype)
+    ref = oracle.decode(raw(q), raw(k0), raw(v0), table, cl, 0.3, **kw)
+    hk, hv = empty_pools(NH, Hkv, D, B, tdt, x, 0.0)
+    out_pairs = np.stack([table[0], np.arange(5)], axis=1).astype(np.int64)
+    hk2, hv2 = oracle.swap_blocks(raw(k0), raw(v0), raw(hk), raw(hv), out_pairs,
+                                  num_kv_heads=Hkv, head_dim=D, block_size=B, dtype=dtype)
+    dk, dv = empty_pools(NB, Hkv, D, B, tdt, x, float("nan"))  # the device blocks were reused
+    new_ids = np.array([0, 11, 4, 2, 9], dtype=np.int64)
+    in_pairs = np.stack([np.arange(5), new_ids], axis=1)
+    dk2, dv2 = oracle.swap_blocks(hk2, hv2, raw(dk), raw(dv), in_pairs, num_kv_heads=Hkv,
+                                  head_dim=D, block_size=B, dtype=dtype)
+    got = oracle.decode(raw(q), dk2, dv2, new_ids[None].astype(np.int32), cl, 0.3, **kw)
+    assert np.array_equal(got, ref)
