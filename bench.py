@@ -45,7 +45,11 @@ WORKLOAD_TEXT = {
                              "1,016-token shared prompt, 112 block copies, bf16",
     "long_ctx": "long-context split decode: 4 seqs, 32 q / 8 kv heads, D 128, B 16, ctx 32K / "
                 "64K / 96K / 128K, 512-token partitions, bf16",
+    "swap_llama3_8b": "preemption by swapping, one layer: the 8 longest sequences of the "
+                      "Llama-3-8B-shaped batch (1,744 blocks of 8 kv heads x 16 tokens x D 128, "
+                      "bf16) out to pinned host memory and back into other free device blocks",
 }
+PEAK_HOST_LINK_GBPS = 64.0  # PCIe 5.0 x16, one direction, published
 
 
 def parse():
@@ -144,6 +148,9 @@ def main():
     pa.load_library()  # fails loudly if libpa.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload.startswith("swap_"):
+        bench_swap(args, dev)
+        return
 
     t_setup = time.time()
     case = workloads.CASES[args.workload](
@@ -310,6 +317,149 @@ def main():
                      "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": "pa_decode (partition + merge kernels)",
                      "bytes_per_launch": int(dec_bytes)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_swap(args, dev):
+    """Swap-out then swap-in of the preempted sequences' blocks, one layer's
+    pool pair per step, rotating over `--layers` device pools and as many
+    pinned host pools.  Each direction is one pa_swap_blocks launch; GPU times
+    come from HIP events on the launch stream, eager launches (each step is
+    two launches of tens of milliseconds).  The host-link ceiling is torch's
+    DMA copy of the same number of bytes as one contiguous pinned buffer."""
+    import torch
+
+    import paged_kv_cache_299_amd as pa
+    from paged_kv_cache_299_amd import workloads
+    from paged_kv_cache_299_amd.layout import block_bytes, kv_cache_shapes
+
+    t_setup = time.time()
+    case = workloads.llama3_8b(fill=False, **({} if args.seed is None else {"seed": args.seed}))
+    plan = workloads.swap_plan(case, num_preempted=8)
+    Hkv, D, B, NB, dt = case.num_kv_heads, case.head_dim, case.block_size, case.num_blocks, \
+        case.dtype
+    n, NH = plan.out_map.shape[0], plan.num_host_blocks
+    moved = 2 * n * block_bytes(Hkv, D, B, dt)          # K and V, one direction
+    k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
+    hk_shape, hv_shape = kv_cache_shapes(NH, Hkv, D, B, dt)
+    gen = torch.Generator(device=dev)
+    L = args.layers
+    dev_pools, host_pools = [], []
+    for layer in range(L):
+        gen.manual_seed(2000 + layer)
+        dev_pools.append(tuple(torch.randn(s_, generator=gen, device=dev).to(dt)
+                               for s_ in (k_shape, v_shape)))
+        host_pools.append(tuple(torch.empty(s_, dtype=dt, pin_memory=True)
+                                for s_ in (hk_shape, hv_shape)))
+    out_map = plan.out_map.to(dev)
+    in_map = plan.in_map.to(dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    stream = torch.cuda.Stream()
+
+    def step(layer, direction):
+        (k, v), (hk, hv) = dev_pools[layer], host_pools[layer]
+        if direction == "out":
+            pa.pa_swap_blocks(k, v, hk, hv, out_map, stream=stream)
+        else:
+            pa.pa_swap_blocks(hk, hv, k, v, in_map, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i % L, "out")
+            step(i % L, "in")
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(i % L, "out")
+            ev[i][1].record(stream)
+            step(i % L, "in")
+            ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out_ms = statistics.median(a.elapsed_time(b) for a, b, _ in ev)
+    in_ms = statistics.median(b.elapsed_time(c) for _, b, c in ev)
+    ms_per_step = wall * 1e3 / args.steps
+
+    # host-link ceiling: one contiguous DMA copy of the same bytes each way
+    dbuf = torch.empty(moved, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    d2h, h2d = [], []
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            e0.record(stream)
+            hbuf.copy_(dbuf, non_blocking=True)
+            e1.record(stream)
+            dbuf.copy_(hbuf, non_blocking=True)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            d2h.append(e0.elapsed_time(e1))
+            h2d.append(e1.elapsed_time(e2))
+    dma_out = moved / (statistics.median(d2h) * 1e-3) / 1e9
+    dma_in = moved / (statistics.median(h2d) * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_reps > 0:
+        import oracle
+        (k, v), (hk, hv) = dev_pools[0], host_pools[0]
+        kh, vh = raw_bits(k.cpu()), raw_bits(v.cpu())
+        hkh, hvh = raw_bits(hk.clone()), raw_bits(hv.clone())
+        code = pa.DTYPE_CODES[dt]
+        times = []
+        for _ in range(args.cpu_reps):
+            t = time.perf_counter()
+            oracle.swap_blocks(kh, vh, hkh, hvh, plan.out_map.numpy(), num_kv_heads=Hkv,
+                               head_dim=D, block_size=B, dtype=code)
+            times.append(time.perf_counter() - t)
+        t_med = statistics.median(times)
+        cpu = {"value": round(moved / t_med / 1e9, 3), "unit": "GB/s", "seconds": round(t_med, 4),
+               "cores": 1, "kind": "oracle",
+               "sample": f"swap-out of the same {n} blocks between host arrays (memcpy per "
+                         f"block, K and V), median of {args.cpu_reps} runs"}
+
+    out_gbps = moved / (out_ms * 1e-3) / 1e9
+    in_gbps = moved / (in_ms * 1e-3) / 1e9
+    value = 2 * moved / (ms_per_step * 1e-3) / 1e9
+    best = max(out_gbps, in_gbps)
+    rec = {
+        "metric": "KV block swap between HBM and pinned host memory: GB/s moved (swap-out + "
+                  "swap-in) at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) pools; the seeded Llama-3-8B-shaped batch's tables)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+                   "blocks": n, "bytes_per_direction": int(moved), "seed": case.seed,
+                   "layers_rotated": L},
+        "swap_out_ms": round(out_ms, 4),
+        "swap_in_ms": round(in_ms, 4),
+        "swap_out_GBps": round(out_gbps, 2),
+        "swap_in_GBps": round(in_gbps, 2),
+        "dma_contiguous_GBps": {"device_to_host": round(dma_out, 2),
+                                "host_to_device": round(dma_in, 2)},
+        "launch": "eager, one pa_swap_blocks launch per direction",
+        "roofline": {"bound": "host link", "achieved": round(best, 2),
+                     "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
+                     "frac": round(best / PEAK_HOST_LINK_GBPS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel ("
+                               + ("swap-out" if out_gbps >= in_gbps else "swap-in") + ")",
+                     "bytes_per_launch": int(moved)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

@@ -162,6 +162,36 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, i
                    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks, int dtype,
                    void *stream);
 
+/*
+ * pa_swap_blocks -- move whole physical blocks between two pool pairs, the
+ * data step of preemption by swapping: when GPU memory runs short, the
+ * scheduler moves a preempted sequence's KV blocks out to a pool in CPU
+ * memory, and back into free GPU blocks when it resumes.
+ *   [論文解説: PagedAttention, 実装のポイント › スケジューラ]
+ *
+ *   src_k, src_v   source pools, num_src_blocks blocks each, read only
+ *   dst_k, dst_v   destination pools, num_dst_blocks blocks each, updated
+ *   block_mapping  int64 [num_pairs][2] = (src block, dst block)
+ * Each pool pair has the layout above with the same num_kv_heads, head_dim,
+ * block_size and dtype; the pools are pointers of the caller, who keeps
+ * ownership.  Every pointer may be device memory or pinned host memory
+ * (hipHostMalloc, or torch's pin_memory): one kernel launch moves every pair,
+ * reading and writing host memory directly over the host link, so swap-out
+ * (device -> host), swap-in (host -> device) and moves within one memory are
+ * the same call.  Copies every kv head and slot of K and V, bit for bit.
+ * Asynchronous on `stream`: host pools must not be touched by the host until
+ * the stream has reached this call.
+ * Preconditions: ids in range; destinations distinct; when source and
+ * destination are the same pools, no destination is also a source.
+ * Errors: PA_ERR_INVALID_ARG for non-positive sizes, null pointers, unknown
+ * dtype, pools not 16-byte aligned, or a pointer to pageable host memory
+ * (checked with hipPointerGetAttributes before anything is enqueued).
+ */
+int pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                   const int64_t *block_mapping, int64_t num_pairs, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_src_blocks, int64_t num_dst_blocks,
+                   int dtype, void *stream);
+
 /* Name of a status code (static string, never NULL). */
 const char *pa_status_str(int status);
 

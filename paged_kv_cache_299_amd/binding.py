@@ -11,6 +11,8 @@ Shapes (see layout.py for the pool format):
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
     (calls pa_decode_ex; shared_blocks sets the PA_DECODE_SHARED_BLOCKS hint)
   pa_copy_blocks(k_cache, v_cache, block_mapping int64 [n,2])
+  pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping int64 [n,2])
+    (each tensor on the GPU or in pinned host memory)
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_copy_blocks", "pa_status_str",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_copy_blocks", "pa_swap_blocks", "pa_status_str",
     "pa_last_error", "pa_decode_workspace_bytes", "pa_release_workspaces", "pa_version",
 )
 
@@ -67,6 +69,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
+    lib.pa_swap_blocks.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I64, I64, I32, P]
+    lib.pa_swap_blocks.restype = I32
     lib.pa_status_str.argtypes = [I32]
     lib.pa_status_str.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -112,7 +116,7 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
+def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor, on_gpu: bool = True):
     _need(k_cache.dim() == 5 and v_cache.dim() == 4,
           "k_cache must be [NB, Hkv, D/x, B, x] and v_cache [NB, Hkv, D, B]")
     NB, Hkv, DX, B, X = k_cache.shape
@@ -121,8 +125,14 @@ def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
     _need(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache shape does not match k_cache")
     _need(k_cache.dtype == v_cache.dtype, "k_cache and v_cache dtypes differ")
     _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
-    _need(k_cache.is_cuda and v_cache.device == k_cache.device, "caches must be on one GPU")
+    if on_gpu:
+        _need(k_cache.is_cuda and v_cache.device == k_cache.device, "caches must be on one GPU")
     return NB, Hkv, D, B
+
+
+def _reachable(t: torch.Tensor, name: str) -> None:
+    _need(t.is_cuda or (t.device.type == "cpu" and t.is_pinned()),
+          f"{name} must be on the GPU or in pinned host memory")
 
 
 def pa_write_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
@@ -178,3 +188,29 @@ def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: 
                                        DTYPE_CODES[k_cache.dtype],
                                        _stream_handle(stream, k_cache.device))
     _check(rc, "pa_copy_blocks")
+
+
+def pa_swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                   dst_v: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """Block src of (src_k, src_v) -> block dst of (dst_k, dst_v) for each
+    (src, dst) row of block_mapping; pools on the GPU or in pinned host memory."""
+    NS, Hkv, D, B = _cache_dims(src_k, src_v, on_gpu=False)
+    ND, Hkv2, D2, B2 = _cache_dims(dst_k, dst_v, on_gpu=False)
+    _need((Hkv, D, B) == (Hkv2, D2, B2) and src_k.dtype == dst_k.dtype,
+          "source and destination pools differ in block format")
+    _need(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2 and block_mapping.is_contiguous(),
+          "block_mapping must be contiguous int64 [n, 2]")
+    tensors = dict(src_k=src_k, src_v=src_v, dst_k=dst_k, dst_v=dst_v,
+                   block_mapping=block_mapping)
+    gpus = {t.device for t in tensors.values() if t.is_cuda}
+    _need(len(gpus) <= 1, "GPU tensors must be on one device")
+    for name, t in tensors.items():
+        _reachable(t, name)
+    device = gpus.pop() if gpus else torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(device):
+        rc = load_library().pa_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v),
+                                           _ptr(block_mapping), block_mapping.shape[0], Hkv, D,
+                                           B, NS, ND, DTYPE_CODES[src_k.dtype],
+                                           _stream_handle(stream, device))
+    _check(rc, "pa_swap_blocks")

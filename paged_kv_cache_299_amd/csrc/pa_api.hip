@@ -83,6 +83,35 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
     return PA_OK;
 }
 
+// The address a kernel uses for p: device memory as it is, pinned host memory
+// (hipHostMalloc; torch's pin_memory) through its device mapping.  Pageable
+// host memory cannot be reached by a kernel: PA_ERR_INVALID_ARG.
+int device_view(const void *p, const char *what, const void **out) {
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e == hipErrorInvalidValue) {  // memory HIP does not know (older runtimes)
+        (void)hipGetLastError();
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_swap_blocks: %s is neither device memory nor pinned host memory", what);
+    }
+    if (e != hipSuccess) return hip_fail(e, "pa_swap_blocks: hipPointerGetAttributes");
+    if (attr.type == hipMemoryTypeHost) {
+        void *dp = nullptr;
+        e = hipHostGetDevicePointer(&dp, const_cast<void *>(p), 0);
+        if (e != hipSuccess || !dp) {
+            (void)hipGetLastError();
+            return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: %s is host memory without a device "
+                        "mapping", what);
+        }
+        *out = dp;
+        return PA_OK;
+    }
+    if (attr.type == hipMemoryTypeUnregistered)
+        return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: %s is pageable host memory", what);
+    *out = p;
+    return PA_OK;
+}
+
 constexpr int kBlock = 16;
 constexpr int kMaxPartition = 1024;  // a unit keeps its table slice in one VGPR per lane
 constexpr int kMaxPartitions = 1 << 16;
@@ -187,9 +216,44 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, i
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
     if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_mapping & 7u))
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pools must be 16-byte aligned");
-    hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs,
-                                            num_blocks, block_bytes, (hipStream_t)stream);
+    hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_mapping,
+                                            num_pairs, num_blocks, num_blocks, block_bytes,
+                                            (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(err, "pa_copy_blocks launch");
+    return PA_OK;
+}
+
+int pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                   const int64_t *block_mapping, int64_t num_pairs, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_src_blocks, int64_t num_dst_blocks,
+                   int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: unknown dtype %d", dtype);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_src_blocks <= 0 || num_dst_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: sizes must be positive");
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * e;
+    if (block_bytes % 16 != 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_swap_blocks: a block of %lld bytes is not a multiple of 16",
+                    (long long)block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping)
+        return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: null pointer");
+    if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v) ||
+        ((uintptr_t)block_mapping & 7u))
+        return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: pools must be 16-byte aligned");
+    const void *d[5];
+    const void *h[5] = {src_k, src_v, dst_k, dst_v, block_mapping};
+    const char *names[5] = {"src_k", "src_v", "dst_k", "dst_v", "block_mapping"};
+    for (int i = 0; i < 5; ++i) {
+        const int rc = device_view(h[i], names[i], &d[i]);
+        if (rc != PA_OK) return rc;
+    }
+    hipError_t err = pa::launch_copy_blocks(d[0], d[1], (void *)d[2], (void *)d[3],
+                                            (const int64_t *)d[4], num_pairs, num_src_blocks,
+                                            num_dst_blocks, block_bytes, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_swap_blocks launch");
     return PA_OK;
 }
 

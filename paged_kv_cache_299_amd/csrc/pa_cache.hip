@@ -92,19 +92,26 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
 }
 
 // grid.y walks the pairs, grid.x the 16-byte runs of one block of one pool.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char *__restrict__ k_cache,
-                                                          char *__restrict__ v_cache,
+// Block src of the source pools goes to block dst of the destination pools.
+// The pools may be the same allocations (copy-on-write: no destination is a
+// source, so no byte is both read and written) or different ones (swapping
+// between device memory and pinned host memory, which the kernel reads and
+// writes directly over the host link, every pair in one launch).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const char *__restrict__ src_k,
+                                                          const char *__restrict__ src_v,
+                                                          char *__restrict__ dst_k,
+                                                          char *__restrict__ dst_v,
                                                           const int64_t *__restrict__ pairs,
-                                                          int64_t num_pairs, int64_t num_blocks,
-                                                          int64_t block_bytes) {
+                                                          int64_t num_pairs, int64_t src_blocks,
+                                                          int64_t dst_blocks, int64_t block_bytes) {
     for (int64_t i = blockIdx.y; i < num_pairs; i += gridDim.y) {
         const int64_t src = pairs[2 * i];
         const int64_t dst = pairs[2 * i + 1];
-        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-        const char *ks = k_cache + src * block_bytes;
-        const char *vs = v_cache + src * block_bytes;
-        char *kd = k_cache + dst * block_bytes;
-        char *vd = v_cache + dst * block_bytes;
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+        const char *ks = src_k + src * block_bytes;
+        const char *vs = src_v + src * block_bytes;
+        char *kd = dst_k + dst * block_bytes;
+        char *vd = dst_v + dst * block_bytes;
         for (int64_t off = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; off < block_bytes;
              off += (int64_t)gridDim.x * blockDim.x * 16) {
             const i32x4 a = ld16(ks + off);
@@ -136,8 +143,9 @@ hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, 
     return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t n,
-                              int64_t NB, int64_t block_bytes, hipStream_t stream) {
+hipError_t launch_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                              const int64_t *pairs, int64_t n, int64_t src_blocks,
+                              int64_t dst_blocks, int64_t block_bytes, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     const int threads = 256;
     int64_t runs = block_bytes / 16;
@@ -145,7 +153,8 @@ hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs
     if (gx > 64) gx = 64;
     int64_t gy = n < 65535 ? n : 65535;
     copy_blocks_kernel<<<dim3((unsigned)gx, (unsigned)gy), dim3(threads), 0, stream>>>(
-        (char *)k_cache, (char *)v_cache, pairs, n, NB, block_bytes);
+        (const char *)src_k, (const char *)src_v, (char *)dst_k, (char *)dst_v, pairs, n,
+        src_blocks, dst_blocks, block_bytes);
     return hipGetLastError();
 }
 

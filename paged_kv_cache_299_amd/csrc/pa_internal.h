@@ -35,7 +35,8 @@ hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, 
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
                            int elem_bytes, hipStream_t stream);
 
-hipError_t launch_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t n,
-                              int64_t NB, int64_t block_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                              const int64_t *pairs, int64_t n, int64_t src_blocks,
+                              int64_t dst_blocks, int64_t block_bytes, hipStream_t stream);
 
 }  // namespace pa

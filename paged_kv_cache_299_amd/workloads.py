@@ -115,6 +115,15 @@ def _tables(bm: BlockManager, seq_ids, MB: int) -> torch.Tensor:
     return torch.tensor(bm.tables(seq_ids, MB), dtype=torch.int32).reshape(len(seq_ids), MB)
 
 
+def random_pools(seed: int, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                 dtype: torch.dtype) -> Tuple[torch.Tensor, torch.Tensor]:
+    """A K and a V pool (CPU) with N(0,1) in every slot: source or
+    destination pools of block moves, where every byte is compared."""
+    rng = np.random.default_rng(seed)
+    k_shape, v_shape = kv_cache_shapes(num_blocks, num_kv_heads, head_dim, block_size, dtype)
+    return _randn(rng, k_shape, dtype), _randn(rng, v_shape, dtype)
+
+
 def make_decode_case(name: str, *, seed: int, context_lens: Sequence[int], num_heads: int,
                      num_kv_heads: int, head_dim: int, block_size: int, num_blocks: int,
                      max_blocks: int, dtype: torch.dtype, partition_tokens: Optional[int] = None,
@@ -256,6 +265,38 @@ def shares_blocks(block_tables: torch.Tensor, context_lens: torch.Tensor, block_
     used = [bt[s, :-(-int(c) // block_size)] for s, c in enumerate(context_lens.tolist())]
     ids = np.concatenate(used) if used else np.zeros(0, dtype=bt.dtype)
     return bool(ids.size) and np.unique(ids).size < ids.size
+
+
+@dataclass
+class SwapPlan:
+    """Preemption by swapping for one decode batch: the preempted sequences'
+    blocks go to a CPU pool (swap-out) and, on resume, come back into free
+    device blocks (swap-in)."""
+    seq_ids: List[int]
+    out_map: torch.Tensor        # int64 [n, 2] (device block, host block)
+    in_map: torch.Tensor         # int64 [n, 2] (host block, new device block)
+    num_host_blocks: int
+
+
+def swap_plan(case: DecodeCase, num_preempted: int, seed: int = 7) -> SwapPlan:
+    """Preempt the num_preempted sequences holding the most blocks; host
+    blocks are handed out in order from an empty CPU pool, and the swap-in
+    targets are blocks no sequence of the case uses, in seeded order."""
+    rng = np.random.default_rng(seed)
+    B = case.block_size
+    nblk = [-(-int(c) // B) for c in case.context_lens.tolist()]
+    order = sorted(range(case.num_seqs), key=lambda s: (-nblk[s], s))[:num_preempted]
+    dev_blocks = [int(b) for s in order for b in case.block_tables[s, :nblk[s]].tolist()]
+    used = {int(b) for s in range(case.num_seqs) for b in case.block_tables[s, :nblk[s]].tolist()}
+    free = np.array(sorted(set(range(case.num_blocks)) - used), dtype=np.int64)
+    n = len(dev_blocks)
+    if n > free.size:
+        raise ValueError("not enough free device blocks to swap the sequences back in")
+    host = np.arange(n, dtype=np.int64)
+    back = rng.permutation(free)[:n]
+    out_map = torch.from_numpy(np.stack([np.array(dev_blocks, dtype=np.int64), host], 1))
+    in_map = torch.from_numpy(np.stack([host, back], 1))
+    return SwapPlan(order, out_map.contiguous(), in_map.contiguous(), n)
 
 
 CASES = {
