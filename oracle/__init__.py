@@ -5,7 +5,7 @@ this package.  The GPU library does not use it in any way.
 """
 from .oracle import (  # noqa: F401
     F32, F16, BF16,
-    decode, decode_partitioned, write_kv, copy_blocks, swap_blocks,
+    decode, decode_partitioned, prefill, write_kv, copy_blocks, swap_blocks,
     kv_cache_bytes, blocks_for_tokens, slot_of,
     f16_bits_to_float64, bf16_bits_to_float64,
     OracleError, num_threads,

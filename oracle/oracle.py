@@ -53,6 +53,9 @@ def _load():
     lib.oracle_decode_partitioned.argtypes = [P, P, P, P, P, D, P, I64, I64, I64, I64, I64, I64,
                                               I64, I64, I32, I64, P, P, P]
     lib.oracle_decode_partitioned.restype = I32
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, P, D, P, I64, I64, I64, I64, I64, I64, I64,
+                                   I64, I64, I32]
+    lib.oracle_prefill.restype = I32
     lib.oracle_write_kv.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32]
     lib.oracle_write_kv.restype = I32
     lib.oracle_copy_blocks.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32]
@@ -114,6 +117,34 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, num_kv_hea
     rc = lib.oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
                            float(scale), _ptr(out), S, Hq, num_kv_heads, D, block_size, MB, NB,
                            k_x, dtype)
+    _check(rc)
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, *,
+            num_kv_heads, head_dim, block_size, k_x, dtype):
+    """fp64 paged prefill: q [T, Hq, D] packed per sequence (query_start [S+1]);
+    the i-th of a sequence's n queries attends over positions 0..ctx-n+i.
+    Returns float64 [T, Hq, D]."""
+    lib = _load()
+    q = _raw(q, dtype)
+    k_cache = _raw(k_cache, dtype)
+    v_cache = _raw(v_cache, dtype)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    S = cl.shape[0]
+    if qs.shape != (S + 1,):
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    T = int(qs[-1]) if S else 0
+    D = head_dim
+    Hq = q.size // max(1, T * D) if T else 1
+    MB = bt.shape[1] if bt.ndim == 2 else 0
+    NB = k_cache.size // (num_kv_heads * block_size * D)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    rc = lib.oracle_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl), _ptr(qs),
+                            float(scale), _ptr(out), S, T, Hq, num_kv_heads, D, block_size, MB,
+                            NB, k_x, dtype)
     _check(rc)
     return out
 

@@ -21,6 +21,12 @@
  *                             in the same section ("online softmax,
  *                             FlashAttention style"), written out for whole
  *                             partitions.
+ *   oracle_prefill            the queries of a chunk of new tokens, each over
+ *                             the cached tokens up to its own position (causal),
+ *                             fetched through the same block table.
+ *                             [論文解説: PagedAttention, 実装のポイント ›
+ *                              CUDAカーネル実装: one kernel for prefill and
+ *                              decode]
  *   oracle_write_kv           scatter of new tokens' K/V into slots
  *                             (slot = physical block * B + offset).
  *   oracle_copy_blocks        copy of whole physical blocks, the copy step of
@@ -36,6 +42,9 @@
  *   - only tokens i < ctx contribute; the rest of the last block is ignored
  *     whatever bits it holds;
  *   - ctx == 0 gives an all-zero output;
+ *   - prefill: the chunk's own K/V are in the pool before the call, the i-th
+ *     of n queries sits at position ctx - n + i and sees positions up to its
+ *     own (causal); q / out rows are packed per sequence (query_start);
  *   - query head h reads kv head h / (Hq / Hkv) (contiguous groups);
  *   - `scale` multiplies the dot products (the page fixes 1/sqrt(d));
  *   - write: slot < 0 means "skip"; non-negative slots must be distinct;
@@ -156,14 +165,14 @@ static int64_t phys_block(const int32_t *block_tables, int64_t s, int64_t MB, in
  * sequence s.  Writes the unnormalised output sum_i w_i v_i with
  * w_i = exp(x_i - m), and returns m = max_i x_i and l = sum_i w_i.  For an
  * empty range m = -inf, l = 0 and the output is zero. */
-static void attend_range(const void *q, const void *k_cache, const void *v_cache,
+static void attend_range(const void *q, int64_t qrow /* element offset of the row */,
+                         const void *k_cache, const void *v_cache,
                          const int32_t *block_tables, double scale, int64_t s, int64_t h,
                          int64_t t0, int64_t t1, int64_t Hq, int64_t Hkv, int64_t D, int64_t B,
                          int64_t MB, int64_t k_x, int dtype, double *x /* scratch [t1-t0] */,
                          double *o /* [D] */, double *m_out, double *l_out) {
     int64_t G = Hq / Hkv;
     int64_t g = h / G;
-    const int64_t qrow = (s * Hq + h) * D;
     double m = -INFINITY;
     for (int64_t i = t0; i < t1; ++i) {
         int64_t b = phys_block(block_tables, s, MB, B, i);
@@ -214,8 +223,57 @@ int oracle_decode(const void *q, const void *k_cache, const void *v_cache,
             continue;
         }
         double m, l;
-        attend_range(q, k_cache, v_cache, block_tables, scale, s, h, 0, n, Hq, Hkv, D, B, MB, k_x,
+        attend_range(q, (s * Hq + h) * D, k_cache, v_cache, block_tables, scale, s, h, 0, n, Hq,
+                     Hkv, D, B, MB, k_x,
                      dtype, x, dst, &m, &l);
+        for (int64_t d = 0; d < D; ++d) dst[d] /= l;
+        free(x);
+    }
+    return failed ? OR_NO_MEM : OR_OK;
+}
+
+/* Paged prefill: the queries of a chunk of new tokens attend causally over
+ * the sequence's cached tokens.  Sequence s owns query rows
+ * query_start[s] .. query_start[s+1]-1 of q and out ([T][Hq][D]); with
+ * n = query_start[s+1] - query_start[s] <= ctx = context_lens[s], its i-th
+ * query is the token at position ctx - n + i, whose K/V are already in the
+ * pool, and it attends over positions 0 .. ctx - n + i (itself included):
+ *   out[t][h] = sum_{j <= p} softmax_j(scale * q.k_j) v_j,  p = ctx - n + i.
+ * n == ctx is a whole prompt, n < ctx a chunk after a cached prefix, n == 1
+ * one decode step.  The same kernel serves both phases.
+ * [論文解説: PagedAttention, 実装のポイント › CUDAカーネル実装; causal
+ *  attention of the new tokens is the standard prefill the page names] */
+int oracle_prefill(const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start, double scale, double *out, int64_t S, int64_t T,
+                   int64_t Hq, int64_t Hkv, int64_t D, int64_t B, int64_t MB, int64_t NB,
+                   int64_t k_x, int dtype) {
+    int rc = check_decode_args(block_tables, context_lens, S, Hq, Hkv, D, B, MB, NB, k_x, dtype);
+    if (rc != OR_OK) return rc;
+    if (T < 0 || (S > 0 && query_start[0] != 0) || (S == 0 && T != 0)) return OR_BAD_DIMS;
+    for (int64_t s = 0; s < S; ++s) {
+        int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+        if (n < 0 || n > context_lens[s]) return OR_BAD_CTX;
+    }
+    if (S > 0 && query_start[S] != T) return OR_BAD_DIMS;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t th = 0; th < T * Hq; ++th) {
+        int64_t t = th / Hq, h = th % Hq;
+        int64_t s = 0;
+        while (query_start[s + 1] <= t) ++s; /* the sequence that owns row t */
+        int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+        int64_t p = context_lens[s] - n + (t - query_start[s]);
+        double *dst = out + th * D;
+        double *x = (double *)malloc(sizeof(double) * (size_t)(p + 1));
+        if (!x) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double m, l;
+        attend_range(q, th * D, k_cache, v_cache, block_tables, scale, s, h, 0, p + 1, Hq, Hkv,
+                     D, B, MB, k_x, dtype, x, dst, &m, &l);
         for (int64_t d = 0; d < D; ++d) dst[d] /= l;
         free(x);
     }
@@ -263,7 +321,8 @@ int oracle_decode_partitioned(const void *q, const void *k_cache, const void *v_
         }
         for (int64_t p = 0; p < np; ++p) {
             int64_t t0 = p * P, t1 = t0 + P < n ? t0 + P : n;
-            attend_range(q, k_cache, v_cache, block_tables, scale, s, h, t0, t1, Hq, Hkv, D, B,
+            attend_range(q, (s * Hq + h) * D, k_cache, v_cache, block_tables, scale, s, h, t0, t1,
+                         Hq, Hkv, D, B,
                          MB, k_x, dtype, x, os + p * D, &ms[p], &ls[p]);
         }
         if (part_m && part_l && part_o) {

@@ -466,3 +466,120 @@ def test_swap_out_and_in_preserves_attention(dtype):
                                   head_dim=D, block_size=B, dtype=dtype)
     got = oracle.decode(raw(q), dk2, dv2, new_ids[None].astype(np.int32), cl, 0.3, **kw)
     assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# paged prefill: causal attention of a chunk of new tokens over the pool
+# --------------------------------------------------------------------------
+def _chunk_queries(rng, ctxs, qlens, Hq, D, dtype):
+    tdt = TORCH_DTYPE[dtype]
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = torch.from_numpy(rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float32)).to(tdt)
+    return q, qs
+
+
+def _oracle_prefill(q, kp, vp, tables, ctx, qs, scale, Hkv, D, B, dtype, x):
+    return oracle.prefill(raw(q), raw(kp), raw(vp), tables, ctx, qs, scale, num_kv_heads=Hkv,
+                          head_dim=D, block_size=B, k_x=x, dtype=dtype)
+
+
+@pytest.mark.parametrize("dtype", [F32, F16, BF16])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (8, 1), (6, 3)])
+def test_prefill_equals_masked_softmax_attention(dtype, Hq, Hkv):
+    """Whole prompts (n = ctx), chunks after a cached prefix (n < ctx), one
+    query (n = 1) and no query (n = 0) against torch's float64 attention with
+    the causal mask written as a boolean matrix: query i of n sees key j iff
+    j <= ctx - n + i."""
+    rng = np.random.default_rng(500 + dtype * 10 + Hq)
+    D, B = 16, 16
+    ctxs = [1, 5, 16, 17, 100, 33, 40]
+    qlens = [1, 5, 7, 17, 30, 0, 1]
+    scale = 1.0 / math.sqrt(D)
+    _, kp, vp, tables, ctx, dense, x = _paged_case(rng, ctxs, Hq, Hkv, D, B, dtype)
+    q, qs = _chunk_queries(rng, ctxs, qlens, Hq, D, dtype)
+    out = _oracle_prefill(q, kp, vp, tables, ctx, qs, scale, Hkv, D, B, dtype, x)
+    G = Hq // Hkv
+    for s, (c, n) in enumerate(zip(ctxs, qlens)):
+        if n == 0:
+            continue
+        qq = q[qs[s]:qs[s + 1]].to(torch.float64).permute(1, 0, 2)[None]        # [1, Hq, n, D]
+        kk = dense[s][0].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()[None]
+        vv = dense[s][1].permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()[None]
+        allowed = (torch.arange(c)[None, :] <= (c - n + torch.arange(n))[:, None])
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=allowed,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[qs[s]:qs[s + 1]], ref[0].permute(1, 0, 2).numpy(),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_brute_force_tiny_shapes():
+    """Tiny geometries against a pure-Python double loop over the logical tokens."""
+    rng = np.random.default_rng(501)
+    for B in (1, 2, 4):
+        for D in (1, 3):
+            for Hq, Hkv in ((1, 1), (2, 1), (2, 2)):
+                ctxs = [int(c) for c in rng.integers(1, 7, size=3)]
+                qlens = [int(rng.integers(0, c + 1)) for c in ctxs]
+                _, kp, vp, tables, ctx, dense, x = _paged_case(rng, ctxs, Hq, Hkv, D, B, F32,
+                                                               x=1)
+                q, qs = _chunk_queries(rng, ctxs, qlens, Hq, D, F32)
+                out = _oracle_prefill(q, kp, vp, tables, ctx, qs, 0.7, Hkv, D, B, F32, 1)
+                for s, (c, n) in enumerate(zip(ctxs, qlens)):
+                    for i in range(n):
+                        p = c - n + i
+                        for h in range(Hq):
+                            g = h // (Hq // Hkv)
+                            qv = [float(q[qs[s] + i, h, d]) for d in range(D)]
+                            sc = [0.7 * sum(qv[d] * float(dense[s][0][j, g, d]) for d in range(D))
+                                  for j in range(p + 1)]
+                            mx = max(sc)
+                            w = [math.exp(a - mx) for a in sc]
+                            for d in range(D):
+                                o = sum(w[j] * float(dense[s][1][j, g, d])
+                                        for j in range(p + 1)) / sum(w)
+                                assert abs(out[qs[s] + i, h, d] - o) <= 1e-12 * (1 + abs(o))
+
+
+def test_prefill_last_query_of_a_chunk_is_the_decode_of_that_token():
+    rng = np.random.default_rng(502)
+    ctxs, qlens = [9, 33, 64, 70], [9, 4, 1, 16]
+    _, kp, vp, tables, ctx, dense, x = _paged_case(rng, ctxs, 8, 2, 16, 16, BF16)
+    q, qs = _chunk_queries(rng, ctxs, qlens, 8, 16, BF16)
+    out = _oracle_prefill(q, kp, vp, tables, ctx, qs, 0.25, 2, 16, 16, BF16, x)
+    last = q[qs[1:] - 1]
+    dec = _oracle_decode(last, kp, vp, tables, ctx, 0.25, 2, 16, 16, BF16, x)
+    assert np.array_equal(out[qs[1:] - 1], dec)
+
+
+def test_prefill_never_reads_past_each_query_position():
+    """Changing the K/V of position j changes exactly the rows at positions >= j."""
+    rng = np.random.default_rng(503)
+    ctxs, qlens = [40, 23], [25, 23]
+    _, kp, vp, tables, ctx, dense, x = _paged_case(rng, ctxs, 4, 2, 16, 4, F32)
+    q, qs = _chunk_queries(rng, ctxs, qlens, 4, 16, F32)
+    a = _oracle_prefill(q, kp, vp, tables, ctx, qs, 0.3, 2, 16, 4, F32, x)
+    j = 30                                    # position 30 of sequence 0: row i = 30 - 15
+    blk, off = tables[0, j // 4], j % 4
+    kp2, vp2 = kp.clone(), vp.clone()
+    kp2[blk, :, :, off, :] += 1.0
+    vp2[blk, :, :, off] -= 2.0
+    b = _oracle_prefill(q, kp2, vp2, tables, ctx, qs, 0.3, 2, 16, 4, F32, x)
+    first = j - (40 - 25)
+    assert np.array_equal(a[:first], b[:first])
+    assert not np.isclose(a[first:25], b[first:25]).all(axis=-1).any()
+    assert np.array_equal(a[25:], b[25:])     # the other sequence
+
+
+@pytest.mark.parametrize("qs,ctx", [
+    ([0, 3, 2], [5, 5]),        # decreasing
+    ([1, 3, 5], [5, 5]),        # does not start at 0
+    ([0, 6, 8], [5, 5]),        # more queries than context
+])
+def test_prefill_rejects_broken_preconditions(qs, ctx):
+    rng = np.random.default_rng(504)
+    _, kp, vp, tables, _, _, x = _paged_case(rng, [5, 5], 2, 1, 8, 4, F32)
+    q = torch.zeros(max(qs[-1], 1), 2, 8)
+    with pytest.raises(OracleError):
+        oracle.prefill(raw(q[:qs[-1]]), raw(kp), raw(vp), tables, np.array(ctx, np.int32),
+                       np.array(qs, np.int32), 0.5, num_kv_heads=1, head_dim=8, block_size=4,
+                       k_x=x, dtype=F32)
