@@ -45,11 +45,17 @@ WORKLOAD_TEXT = {
                              "1,016-token shared prompt, 112 block copies, bf16",
     "long_ctx": "long-context split decode: 4 seqs, 32 q / 8 kv heads, D 128, B 16, ctx 32K / "
                 "64K / 96K / 128K, 512-token partitions, bf16",
+    "prefill_llama3_8b": "paged prefill, one layer: 8 whole prompts of U{1024..4096} tokens "
+                         "(21,069 tokens), 32 q / 8 kv heads, D 128, B 16, bf16",
+    "prefill_chunked_llama3_8b": "chunked paged prefill, one layer: 8 sequences with cached "
+                                 "prefixes of U{0..15360} tokens take 1,024-token chunks, "
+                                 "32 q / 8 kv heads, D 128, B 16, bf16",
     "swap_llama3_8b": "preemption by swapping, one layer: the 8 longest sequences of the "
                       "Llama-3-8B-shaped batch (1,744 blocks of 8 kv heads x 16 tokens x D 128, "
                       "bf16) out to pinned host memory and back into other free device blocks",
 }
 PEAK_HOST_LINK_GBPS = 64.0  # PCIe 5.0 x16, one direction, published
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix cores, published
 
 
 def parse():
@@ -150,6 +156,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload.startswith("swap_"):
         bench_swap(args, dev)
+        return
+    if args.workload.startswith("prefill_"):
+        bench_prefill(args, dev)
         return
 
     t_setup = time.time()
@@ -317,6 +326,177 @@ def main():
                      "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": "pa_decode (partition + merge kernels)",
                      "bytes_per_launch": int(dec_bytes)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def contiguous_tables(case):
+    """The same sequences with each one's blocks at consecutive physical ids
+    (what a contiguous KV layout would read), for the paging-overhead figure."""
+    import torch
+    B = case.block_size
+    tables = torch.zeros_like(case.block_tables)
+    nxt = 0
+    for s, c in enumerate(case.context_lens.tolist()):
+        nb = -(-c // B)
+        tables[s, :nb] = torch.arange(nxt, nxt + nb, dtype=torch.int32)
+        nxt += nb
+    if nxt > case.num_blocks:
+        raise ValueError("pool too small for a contiguous layout")
+    return tables
+
+
+def bench_prefill(args, dev):
+    """A step is one layer of a prefill iteration: pa_write_kv of every new
+    token's K/V into its slot, then pa_prefill.  Steps rotate over `--layers`
+    pool pairs and run as HIP graph replays (one graph per pass over the
+    layers).  `value` = useful causal flops of the step / step time; the
+    roofline covers pa_prefill alone against the dense bf16 matrix-core peak."""
+    import torch
+
+    import paged_kv_cache_299_amd as pa
+    from paged_kv_cache_299_amd import workloads
+    from paged_kv_cache_299_amd.layout import kv_cache_shapes
+
+    t_setup = time.time()
+    case = workloads.CASES[args.workload](
+        fill=False, **({} if args.seed is None else {"seed": args.seed}))
+    Hq, Hkv, D, B, NB, dt = case.num_heads, case.num_kv_heads, case.head_dim, \
+        case.block_size, case.num_blocks, case.dtype
+    T, S, MQ = case.q.shape[0], case.num_seqs, case.max_query_len
+    flops = workloads.prefill_flops(case)
+    k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
+    gen = torch.Generator(device=dev)
+    pools = []
+    for layer in range(args.layers):
+        gen.manual_seed(3000 + 100 * case.seed + layer)
+        pools.append(tuple(torch.randn(s_, generator=gen, device=dev).to(dt)
+                           for s_ in (k_shape, v_shape)))
+    q = case.q.to(dev)
+    bt = case.block_tables.to(dev)
+    bt_contig = contiguous_tables(case).to(dev)
+    cl = case.context_lens.to(dev)
+    qs = case.query_start.to(dev)
+    out = torch.empty_like(q)
+    st = case.write_step
+    k_new, v_new, slots = st.k_new.to(dev), st.v_new.to(dev), st.slot_mapping.to(dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    L = len(pools)
+    stream = torch.cuda.Stream()
+
+    def enqueue(layer, write=True, attend=True, tables=bt):
+        k, v = pools[layer]
+        if write:
+            pa.pa_write_kv(k_new, v_new, k, v, slots)
+        if attend:
+            pa.pa_prefill(q, k, v, tables, cl, qs, case.scale, out, max_query_len=MQ)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            enqueue(i % L)
+    torch.cuda.synchronize()
+
+    def timed(n, **phase):
+        q_, r_ = divmod(n, L)
+        graphs = []
+        for layers in ([range(L)] * (1 if q_ else 0)) + ([range(r_)] if r_ else []):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for l in layers:
+                    enqueue(l, **phase)
+            graphs.append(g)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(q_):
+                graphs[0].replay()
+            if r_:
+                graphs[-1].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1)
+
+    wall, _ = timed(args.steps)
+    ms_per_step = wall * 1e3 / args.steps
+    _, pf_ms = timed(args.steps, write=False)
+    _, wr_ms = timed(args.steps, attend=False)
+    _, pc_ms = timed(args.steps, write=False, tables=bt_contig)
+    pf_avg, wr_avg, pc_avg = pf_ms / args.steps, wr_ms / args.steps, pc_ms / args.steps
+    achieved = flops / (pf_avg * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if args.cpu_reps > 0:
+        import numpy as np
+        import oracle
+        k0, v0 = pools[0]
+        with torch.cuda.stream(stream):
+            enqueue(0)
+        torch.cuda.synchronize()
+        kh, vh = raw_bits(k0.cpu()), raw_bits(v0.cpu())
+        # sampled rows: query i of a chunk of n is the decode of position
+        # ctx - n + i over its first ctx - n + i + 1 tokens
+        rng = np.random.default_rng(0)
+        qs_h = case.query_start.tolist()
+        rows, ctx_at, seq_of = [], [], []
+        for s, (c, n) in enumerate(zip(case.context_lens.tolist(), case.query_lens)):
+            for i in rng.choice(n, size=min(n, 16), replace=False).tolist():
+                rows.append(qs_h[s] + i)
+                ctx_at.append(c - n + i + 1)
+                seq_of.append(s)
+        sample_flops = 4 * D * Hq * sum(ctx_at)
+        times = []
+        for _ in range(args.cpu_reps):
+            t = time.perf_counter()
+            oracle.decode(raw_bits(case.q[rows]), kh, vh, case.block_tables.numpy()[seq_of],
+                          np.array(ctx_at, np.int32), case.scale, num_kv_heads=Hkv, head_dim=D,
+                          block_size=B, k_x=16 // torch.tensor([], dtype=dt).element_size(),
+                          dtype=pa.DTYPE_CODES[dt])
+            times.append(time.perf_counter() - t)
+        t_med = statistics.median(times)
+        cpu = {"value": round(sample_flops / t_med / 1e12, 6), "unit": "TFLOP/s",
+               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{len(rows)} query rows (16 per sequence, all {Hq} heads) of layer 0, "
+                         f"each over its causal prefix, median of {args.cpu_reps} runs, fp64"}
+        del kh, vh
+
+    rec = {
+        "metric": "paged prefill attention: useful causal TFLOP/s at 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded block placement and prompt lengths)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+                   "num_seqs": S, "num_tokens": T, "num_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": B, "num_blocks": NB, "seed": case.seed,
+                   "max_query_len": MQ, "context_tokens": int(case.context_lens.sum()),
+                   "layers_rotated": L},
+        "flops_per_step": int(flops),
+        "prefill_us": round(pf_avg * 1e3, 2),
+        "write_us": round(wr_avg * 1e3, 2),
+        "prefill_contiguous_blocks_us": round(pc_avg * 1e3, 2),
+        "paging_overhead_pct": round(100 * (pf_avg / pc_avg - 1), 2),
+        "launch": "HIP graph replays, one graph per pass over the rotated layers",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "pa_prefill (prefill_mfma_kernel)",
+                     "flops_per_launch": int(flops)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

@@ -144,6 +144,42 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int partition_tokens, int flags, void *stream);
 
 /*
+ * pa_prefill -- paged prefill attention: the queries of a chunk of new tokens
+ * attend causally over their sequence's tokens in the pool.  The same block
+ * gather as decode serves the prefill phase.
+ *   [論文解説: PagedAttention, 実装のポイント › CUDAカーネル実装]
+ *
+ *   q, out         [num_tokens][num_heads][D], device; the rows of sequence s
+ *                  are query_start[s] .. query_start[s+1]-1 (packed, in order)
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq], device
+ *   context_lens   int32 [num_seqs], device: tokens of the sequence in the
+ *                  pool, the chunk's own included (write them with
+ *                  pa_write_kv first)
+ *   query_start    int32 [num_seqs + 1], device, query_start[0] = 0,
+ *                  query_start[num_seqs] = num_tokens
+ *   max_query_len  host bound on query_start[s+1] - query_start[s] (sizes the
+ *                  launch grid)
+ * With n = query_start[s+1] - query_start[s] <= ctx = context_lens[s], query
+ * i of sequence s is the token at position ctx - n + i and its output is
+ *   sum_{j <= ctx - n + i} softmax_j(scale * q . k_j) v_j.
+ * n = ctx is a whole prompt, n < ctx a chunk after a cached prefix, n = 0
+ * leaves the sequence out.  bf16 and fp16; fp32 is PA_ERR_UNSUPPORTED.
+ * Arithmetic: scores and the softmax in fp32; P.V on the matrix cores with
+ * each weight split into two 16-bit parts (hi + lo), fp32 accumulation.
+ * Preconditions (device values): query_start non-decreasing, n <= ctx,
+ * ctx <= max_blocks_per_seq * 16, block ids in range.
+ * Errors: PA_ERR_INVALID_ARG for bad sizes, dtype, scale, pointers, or
+ * max_query_len > num_tokens; PA_ERR_UNSUPPORTED for fp32, block_size != 16,
+ * head_dim not 64 or 128, or a grid past the launch limits (num_seqs > 65535).
+ * Allocates nothing.
+ */
+int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, float scale, void *out, int num_seqs, int num_tokens,
+               int max_query_len, int num_heads, int num_kv_heads, int head_dim, int block_size,
+               int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks, the copy step of
  * copy-on-write: a block shared by several sequences (reference count > 1) is
  * copied to a fresh block before one of them writes into it.

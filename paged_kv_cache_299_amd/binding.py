@@ -10,6 +10,8 @@ Shapes (see layout.py for the pool format):
   pa_decode(q [S,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
     (calls pa_decode_ex; shared_blocks sets the PA_DECODE_SHARED_BLOCKS hint)
+  pa_prefill(q [T,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
+             query_start int32 [S+1], scale, out [T,Hq,D], max_query_len=None)
   pa_copy_blocks(k_cache, v_cache, block_mapping int64 [n,2])
   pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping int64 [n,2])
     (each tensor on the GPU or in pinned host memory)
@@ -33,7 +35,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_copy_blocks", "pa_swap_blocks", "pa_status_str",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_prefill", "pa_copy_blocks", "pa_swap_blocks",
+    "pa_status_str",
     "pa_last_error", "pa_decode_workspace_bytes", "pa_release_workspaces", "pa_version",
 )
 
@@ -69,6 +72,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
+    lib.pa_prefill.argtypes = [P, P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I32, I32,
+                               I64, I32, P]
+    lib.pa_prefill.restype = I32
     lib.pa_swap_blocks.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I64, I64, I32, P]
     lib.pa_swap_blocks.restype = I32
     lib.pa_status_str.argtypes = [I32]
@@ -174,6 +180,39 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+               scale: float, out: torch.Tensor, max_query_len: Optional[int] = None,
+               stream=None) -> None:
+    """Causal attention of each sequence's new queries (rows query_start[s] ..
+    query_start[s+1]-1 of q) over its context_lens[s] tokens in the pool.
+    max_query_len: a bound on the queries per sequence; None reads it from
+    query_start (a device-to-host copy)."""
+    NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == D and q.shape == out.shape,
+          "q and out must be [T, Hq, D] with the caches' D")
+    _need(q.dtype == k_cache.dtype == out.dtype, "q, caches and out differ in dtype")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    S = context_lens.shape[0]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(),
+          "context_lens must be contiguous int32 [S]")
+    _need(query_start.dtype == torch.int32 and tuple(query_start.shape) == (S + 1,)
+          and query_start.is_contiguous(), "query_start must be contiguous int32 [S + 1]")
+    for t in (q, out, block_tables, context_lens, query_start):
+        _need(t.device == k_cache.device, "all tensors must be on the caches' GPU")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
+    rc = load_library().pa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(context_lens), _ptr(query_start), float(scale), _ptr(out),
+                                   S, q.shape[0], int(max_query_len), q.shape[1], Hkv, D, B,
+                                   block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
+                                   _stream_handle(stream, k_cache.device))
+    _check(rc, "pa_prefill")
 
 
 def pa_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor,

@@ -374,6 +374,70 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
                         num_blocks, dtype, 0, 0, stream);
 }
 
+int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, float scale, void *out, int num_seqs, int num_tokens,
+               int max_query_len, int num_heads, int num_kv_heads, int head_dim, int block_size,
+               int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_prefill: unknown dtype %d", dtype);
+    if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_prefill: sizes must be positive");
+    if (num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_prefill: num_heads %d is not a multiple of %d",
+                    num_heads, num_kv_heads);
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_prefill: scale is not finite");
+    if (max_query_len > num_tokens)
+        return fail(PA_ERR_INVALID_ARG, "pa_prefill: max_query_len %d exceeds num_tokens %d",
+                    max_query_len, num_tokens);
+    if (dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: fp32 (the matrix-core path takes 16-bit "
+                    "data)");
+    if (block_size != kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d (only 16 is built)",
+                    block_size);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (64 and 128 are built)",
+                    head_dim);
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: max_blocks_per_seq too large");
+    const int G = num_heads / num_kv_heads;
+    if ((int64_t)max_query_len * G > (int64_t)1 << 30 || num_seqs > 65535 ||
+        pa::prefill_row_tiles(max_query_len, G) > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d sequences x %d queries x %d heads per "
+                    "kv head exceed the launch grid", num_seqs, max_query_len, G);
+    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return fail(PA_ERR_INVALID_ARG, "pa_prefill: null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+        ((uintptr_t)query_start & 3u))
+        return fail(PA_ERR_INVALID_ARG, "pa_prefill: data pointers must be 16-byte aligned");
+
+    pa::PrefillArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.bt = block_tables;
+    a.ctx = context_lens;
+    a.qs = query_start;
+    a.out = out;
+    a.scale_log2_abs = fabsf(scale) * 1.4426950408889634f;
+    a.q_xor = scale < 0.f ? (int)0x80008000u : 0;
+    a.S = num_seqs;
+    a.T = num_tokens;
+    a.Hq = num_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.MB = max_blocks_per_seq;
+    a.NB = num_blocks;
+    hipError_t err = pa::launch_prefill(a, dtype, head_dim, max_query_len, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_prefill launch");
+    return PA_OK;
+}
+
 int pa_release_workspaces(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     int rc = PA_OK;

@@ -38,58 +38,6 @@
 
 namespace pa {
 
-constexpr int kB = 16;  // tokens per block (the only block size these kernels take)
-
-// ---------------------------------------------------------------------------
-// MFMA helper: D = A . B + C on v_mfma_f32_16x16x32 (bf16 or f16).  Lane l
-// supplies A[l % 16][8 (l / 16) .. +8] and B[8 (l / 16) .. +8][l % 16] and
-// receives D[4 (l / 16) .. +4][l % 16] (checked on the hardware).
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ f32x4 mfma32(const i32x4 &a, const i32x4 &b, const f32x4 &c) {
-    if constexpr (DT == kBF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-}
-
-template <int DT> __device__ __forceinline__ float from_bits16(uint32_t b) {
-    return DT == kBF16 ? bf16_lo(b) : f16_lo(b);
-}
-
-// Store 4 consecutive outputs (fp32 values times `mul`) in the output type.
-template <int DT> __device__ __forceinline__ void store4(void *dst, const f32x4 &v, float mul) {
-    if constexpr (DT == kF32) {
-        *(f32x4 *)dst = v * mul;
-    } else {
-        const uint32_t a = to_bits16<DT>(v[0] * mul) | ((uint32_t)to_bits16<DT>(v[1] * mul) << 16);
-        const uint32_t b = to_bits16<DT>(v[2] * mul) | ((uint32_t)to_bits16<DT>(v[3] * mul) << 16);
-        *(i32x2 *)dst = i32x2{(int)a, (int)b};
-    }
-}
-
-template <int DT> __device__ __forceinline__ void store1(void *dst, float v) {
-    if constexpr (DT == kF32) {
-        *(float *)dst = v;
-    } else {
-        *(uint16_t *)dst = to_bits16<DT>(v);
-    }
-}
-
-// Placed right after a prefetch.  The empty asm (no instruction) keeps the
-// optimiser from merging the loads of the loop's first block with those of
-// the next-block prefetch into one load at the loop head; the scheduling
-// barrier keeps the instruction scheduler from sinking the prefetch below the
-// reduction of the current block.  Without them no block would be in flight
-// while the current one is reduced.
-__device__ __forceinline__ void issue_point() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // Clamp a context length read from the device to what the block table holds.
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 

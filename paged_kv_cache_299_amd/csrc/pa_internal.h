@@ -31,6 +31,27 @@ enum class DecodeKernel { kValu, kMfma };
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, DecodeKernel kind,
                          hipStream_t stream);
 
+// Everything one prefill launch needs (16-bit data, B = 16).
+struct PrefillArgs {
+    const void *q;          // [T][Hq][D], rows of sequence s at qs[s] .. qs[s+1]-1
+    const void *k;          // K pool [NB][Hkv][D/x][B][x]
+    const void *v;          // V pool [NB][Hkv][D][B]
+    const int *bt;          // [S][MB]
+    const int *ctx;         // [S]
+    const int *qs;          // [S+1]
+    void *out;              // [T][Hq][D]
+    float scale_log2_abs;   // |scale| * log2(e)
+    int q_xor;              // 0x80008000 when scale < 0
+    int S, T, Hq, Hkv, G, MB;
+    int64_t NB;
+};
+
+// Workgroup rows along the query axis for max_query_len queries of G heads.
+int64_t prefill_row_tiles(int64_t max_query_len, int G);
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int max_query_len,
+                          hipStream_t stream);
+
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
                            int elem_bytes, hipStream_t stream);

@@ -1,0 +1,282 @@
+// pa_prefill.hip -- paged prefill attention on the matrix cores (gfx950).
+//
+// The queries of a chunk of new tokens attend causally over their sequence's
+// cached tokens, read through the block table: the i-th of n queries of a
+// sequence with ctx cached tokens (the chunk's own K/V included) sits at
+// position ctx - n + i and sees positions 0 .. ctx - n + i.  n == ctx is a
+// whole prompt, n < ctx a chunk after a cached prefix, n == 1 a decode step.
+// [論文解説: PagedAttention, 実装のポイント › CUDAカーネル実装: one kernel
+//  gathers the scattered blocks for both the prefill and the decode phase]
+//
+// Work: a workgroup of 4 waves takes 128 consecutive "rows" of one
+// (sequence, kv head); row r is query r / G of the chunk with query head
+// r % G of the group, so the G heads that share a kv head share every K/V
+// operand.  Each wave owns 32 rows as two 16-row tiles and walks the keys 32
+// at a time (two blocks), up to its last row's position.
+//
+// Per 32 keys and 16-row tile, with lane l = 16 j + n:
+//  * S^T = K . Q^T on v_mfma_f32_16x16x32 (4 per block at D = 128): the A
+//    operand is the K tile's 16-byte run 4c + j of token n, read straight from
+//    the pool (64 lanes read 1 KiB in order), the B operand the row's q.  Lane
+//    l receives keys 4j .. 4j+3 of the block for row n.
+//  * online softmax per row (log2 domain, lazy rescale when the maximum grows
+//    by more than 8), causal and tail masking only in the iterations that
+//    need it;
+//  * O^T += V^T . P^T on v_mfma_f32_16x16x32 over the 32 keys: the k slots
+//    8j .. 8j+7 of lane group j hold keys 4j .. 4j+3 of the first block and of
+//    the second block, which is exactly what the lane holds of P^T, and the
+//    A operand is two 8-byte reads of the transposed V tiles at the same
+//    keys.  The weights go in as hi + lo 16-bit parts (hi = RNE(p),
+//    lo = RNE(p - hi)), so P keeps about 16 significant bits.
+// K/V are loaded one iteration ahead with plain (cacheable) loads: the other
+// waves of the workgroup and the other row tiles of the sequence read the
+// same tiles.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPrefillWaves = 4;
+constexpr int kRowTiles = 2;                                 // 16-row tiles per wave
+constexpr int kRowsPerWave = 16 * kRowTiles;                 // 32
+constexpr int kRowsPerGroup = kPrefillWaves * kRowsPerWave;  // 128
+constexpr int kBtChunk = 64;                                 // table entries per lane load
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+    static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
+    static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    constexpr int NKC = D / 32;       // QK steps of 32 dims
+    constexpr int NVT = D / 16;       // output tiles of 16 dims
+    constexpr int TILE = D * kB * 2;  // bytes of one (block, kv head) tile
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
+    const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles first
+
+    // The sequence's queries and context, clamped so that no access leaves
+    // the buffers whatever the device holds.
+    int q0 = __builtin_amdgcn_readfirstlane(a.qs[s]);
+    int q1 = __builtin_amdgcn_readfirstlane(a.qs[s + 1]);
+    q0 = min(max(q0, 0), a.T);
+    q1 = min(max(q1, q0), a.T);
+    int ctx = __builtin_amdgcn_readfirstlane(a.ctx[s]);
+    ctx = min(max(ctx, 0), a.MB * kB);
+    const int nq = min(q1 - q0, ctx);
+    const int rows = nq * a.G;
+    const int R0 = tile * kRowsPerGroup + wave * kRowsPerWave;
+    if (R0 >= rows) return;
+    const int pos0 = ctx - nq;  // position of the chunk's first query
+
+    // this lane's rows: a row past the end repeats the last one (computed, never stored)
+    int prow[kRowTiles];
+    int64_t orow[kRowTiles];
+    bool keep[kRowTiles];
+    i32x4 qf[kRowTiles][NKC];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+        const int R = R0 + 16 * rt + n;
+        const int Rc = min(R, rows - 1);
+        const int ql = Rc / a.G;
+        const int hl = Rc - ql * a.G;
+        prow[rt] = pos0 + ql;
+        orow[rt] = ((int64_t)(q0 + ql) * a.Hq + g * a.G + hl) * D;
+        keep[rt] = R < rows;
+        const uint16_t *qp = (const uint16_t *)a.q + orow[rt];
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) qf[rt][c] = ld16(qp + (4 * c + j) * 8) ^ a.q_xor;
+    }
+    const float cs = a.scale_log2_abs;  // the sign of the scale went into q
+
+    // keys this wave needs: positions 0 .. p_max; no row masks keys <= p_min
+    const int p_min = pos0 + R0 / a.G;
+    const int p_max = pos0 + (min(R0 + kRowsPerWave, rows) - 1) / a.G;
+    const int nblk = p_max / kB + 1;
+    const int iters = (nblk + 1) / 2;
+
+    const char *kbase = (const char *)a.k + (int64_t)g * TILE;
+    const char *vbase = (const char *)a.v + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+    const int *btrow = a.bt + (int64_t)s * a.MB;
+    int my_bt = 0;  // table entries kBtChunk * chunk + lane
+
+    float m[kRowTiles], l[kRowTiles];
+    f32x4 o[kRowTiles][NVT];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+        m[rt] = -INFINITY;
+        l[rt] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    struct Ops {
+        i32x4 k[2][NKC];
+        i32x2 v[2][NVT];
+    };
+    Ops b0, b1;
+    // Iteration it reads blocks 2 it and 2 it + 1; a block past the wave's
+    // last one gets a zero-range descriptor (zeros, no memory traffic).
+    auto load = [&](Ops &x, int it) {
+        if ((it & (kBtChunk / 2 - 1)) == 0) {  // next slice of the block table
+            const int e = 2 * it + lane;
+            int id = e < nblk ? btrow[e] : 0;
+            if (id < 0 || (int64_t)id >= a.NB) id = 0;
+            my_bt = id;
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int blk = 2 * it + b;
+            const bool in = blk < nblk;
+            const int phys = __builtin_amdgcn_readlane(my_bt, in ? (blk & (kBtChunk - 1)) : 0);
+            const int64_t off = (int64_t)phys * blk_stride;
+            const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
+#pragma unroll
+            for (int c = 0; c < NKC; ++c)
+                x.k[b][c] = bload16<kCachePolicyPlain>(rk, (64 * c + lane) * 16);
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+                x.v[b][t] = bload8<kCachePolicyPlain>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+        }
+        issue_point();
+    };
+
+    auto step = [&](Ops &x, Ops &y, int it) {
+        f32x4 sc[kRowTiles][2];
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                sc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NKC; ++c) sc[rt][b] = mfma32<DT>(x.k[b][c], qf[rt][c], sc[rt][b]);
+            }
+        load(y, it + 1);
+        const int key0 = 32 * it;
+        // slots at or past ctx (the tail of the sequence's last block) may hold
+        // NaN: their V is zeroed, since a zero weight does not cancel a NaN
+        if (key0 + 32 > ctx) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int kb = key0 + 16 * b + 4 * j;
+                const uint32_t m0 = (kb + 0 < ctx ? 0x0000ffffu : 0u) | (kb + 1 < ctx ? 0xffff0000u : 0u);
+                const uint32_t m1 = (kb + 2 < ctx ? 0x0000ffffu : 0u) | (kb + 3 < ctx ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int t = 0; t < NVT; ++t)
+                    x.v[b][t] = i32x2{(int)((uint32_t)x.v[b][t][0] & m0),
+                                      (int)((uint32_t)x.v[b][t][1] & m1)};
+            }
+        }
+        i32x4 va[NVT];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t)
+            va[t] = i32x4{x.v[0][t][0], x.v[0][t][1], x.v[1][t][0], x.v[1][t][1]};
+        const bool full = key0 + 31 <= p_min;  // no key of the iteration is masked for any row
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) {
+            float sv[8];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[4 * b + e] = sc[rt][b][e];
+            if (!full) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (key0 + 16 * b + 4 * j + e > prow[rt]) sv[4 * b + e] = -INFINITY;
+            }
+            float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            bm = xor32_max(xor16_max(bm)) * cs;  // -inf when the row sees none of these keys
+            const bool grow = bm > m[rt] + 8.f;
+            if (__any(grow)) {
+                const float mn = grow ? bm : m[rt];
+                const float alpha = fast_exp2(m[rt] - mn);  // 0 on a row's first keys
+#pragma unroll
+                for (int t = 0; t < NVT; ++t) o[rt][t] *= alpha;
+                l[rt] *= alpha;
+                m[rt] = mn;
+            }
+            const float nm = -m[rt];
+            float pe[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(fmaf(sv[e], cs, nm));
+            if (!full) {  // (-inf) * 0 is NaN when the scale is 0
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (key0 + 16 * b + 4 * j + e > prow[rt]) pe[4 * b + e] = 0.f;
+            }
+            l[rt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                hi[w] = pack2<DT>(pe[2 * w], pe[2 * w + 1]);
+                lo[w] = pack2<DT>(pe[2 * w] - elem_lo<DT>(hi[w]), pe[2 * w + 1] - elem_hi<DT>(hi[w]));
+            }
+            const i32x4 phi = {(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const i32x4 plo = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+                o[rt][t] = mfma32<DT>(va[t], phi, o[rt][t]);
+                o[rt][t] = mfma32<DT>(va[t], plo, o[rt][t]);
+            }
+        }
+    };
+
+    // one exit, at the loop test (see the decode kernel)
+    load(b0, 0);
+    int it = 0;
+    for (; it + 2 <= iters; it += 2) {
+        step(b0, b1, it);
+        step(b1, b0, it + 1);
+    }
+    if (it < iters) step(b0, b1, it);
+
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+        const float lt = xor32_sum(xor16_sum(l[rt]));  // all lanes take part in the swaps
+        if (keep[rt]) {
+            const float inv = 1.f / lt;
+            uint16_t *op = (uint16_t *)a.out + orow[rt];
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) store4<DT>(op + 16 * t + 4 * j, o[rt][t], inv);
+        }
+    }
+}
+
+template <int DT>
+hipError_t launch_typed(const PrefillArgs &a, int head_dim, dim3 grid, hipStream_t stream) {
+    if (head_dim == 128) {
+        prefill_mfma_kernel<DT, 128><<<grid, dim3(64 * kPrefillWaves), 0, stream>>>(a);
+    } else {
+        prefill_mfma_kernel<DT, 64><<<grid, dim3(64 * kPrefillWaves), 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t prefill_row_tiles(int64_t max_query_len, int G) {
+    return (max_query_len * G + kRowsPerGroup - 1) / kRowsPerGroup;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int max_query_len,
+                          hipStream_t stream) {
+    const int64_t tiles = prefill_row_tiles(max_query_len, a.G);
+    if (tiles == 0 || a.S == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.Hkv, (unsigned)a.S, (unsigned)tiles);
+    return dtype == kBF16 ? launch_typed<kBF16>(a, head_dim, grid, stream)
+                          : launch_typed<kF16>(a, head_dim, grid, stream);
+}
+
+}  // namespace pa

@@ -268,6 +268,115 @@ def shares_blocks(block_tables: torch.Tensor, context_lens: torch.Tensor, block_
 
 
 @dataclass
+class PrefillCase:
+    """Prefill of a chunk of new tokens per sequence: the chunk's K/V are
+    written into their slots (write_step), then every new query attends
+    causally over its sequence's tokens."""
+    name: str
+    dtype: torch.dtype
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks: int
+    q: torch.Tensor              # [T, Hq, D], the chunks packed in sequence order
+    k_cache: torch.Tensor        # K pool holding the cached prefixes
+    v_cache: torch.Tensor        # V pool holding the cached prefixes
+    block_tables: torch.Tensor   # int32 [S, MB]
+    context_lens: torch.Tensor   # int32 [S], prefix + chunk
+    query_start: torch.Tensor    # int32 [S + 1]
+    scale: float
+    write_step: Optional[WriteStep]
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def query_lens(self) -> List[int]:
+        qs = self.query_start.tolist()
+        return [qs[i + 1] - qs[i] for i in range(self.num_seqs)]
+
+    @property
+    def max_query_len(self) -> int:
+        return max(self.query_lens, default=0)
+
+
+def make_prefill_case(name: str, *, seed: int, context_lens: Sequence[int],
+                      query_lens: Sequence[int], num_heads: int, num_kv_heads: int,
+                      head_dim: int, block_size: int, num_blocks: int, max_blocks: int,
+                      dtype: torch.dtype, rng: Optional[np.random.Generator] = None,
+                      fill: bool = True) -> PrefillCase:
+    """Sequence s holds context_lens[s] - query_lens[s] cached tokens; its
+    query_lens[s] new tokens get slots appended by the block manager, their
+    K/V go in with one write step, and their queries are packed into q."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    S, B = len(context_lens), block_size
+    ctx = [int(c) for c in context_lens]
+    ql = [int(n) for n in query_lens]
+    if len(ql) != S or any(n < 0 or n > c for n, c in zip(ql, ctx)):
+        raise ValueError("need 0 <= query_lens[s] <= context_lens[s]")
+    if any(-(-c // B) > max_blocks for c in ctx):
+        raise ValueError("a context does not fit max_blocks")
+    bm = BlockManager(num_blocks, B, free_order=rng.permutation(num_blocks))
+    for s in range(S):
+        bm.allocate(s, ctx[s] - ql[s])
+    k, v = (_fill_pools(rng, bm, range(S), num_kv_heads, head_dim, B, num_blocks, dtype)
+            if fill else (None, None))
+    slots = []
+    for s in range(S):
+        for _ in range(ql[s]):
+            slots.append(bm.append_slot(s)[0])
+    T = len(slots)
+    q = _randn(rng, (T, num_heads, head_dim), dtype)
+    step = WriteStep(_randn(rng, (T, num_kv_heads, head_dim), dtype),
+                     _randn(rng, (T, num_kv_heads, head_dim), dtype),
+                     torch.tensor(slots, dtype=torch.int64)) if T else None
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(ql)]), dtype=torch.int32)
+    return PrefillCase(name, dtype, S, num_heads, num_kv_heads, head_dim, B, num_blocks,
+                       max_blocks, q, k, v, _tables(bm, range(S), max_blocks),
+                       torch.tensor(ctx, dtype=torch.int32), qs, 1.0 / math.sqrt(head_dim),
+                       step, seed)
+
+
+def prefill_llama3_8b(seed: int = 6, fill: bool = True) -> PrefillCase:
+    """Whole prompts, Llama-3-8B-shaped attention: 8 prompts of U{1024..4096}
+    tokens, 32 query / 8 kv heads, D 128, bf16."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1024, 4096, size=8, endpoint=True)
+    return make_prefill_case("prefill_llama3_8b", seed=seed, context_lens=ctx, query_lens=ctx,
+                             num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                             num_blocks=4096, max_blocks=256, dtype=torch.bfloat16, rng=rng,
+                             fill=fill)
+
+
+def prefill_chunked_llama3_8b(seed: int = 7, fill: bool = True) -> PrefillCase:
+    """Chunked prefill: 8 sequences with cached prefixes of U{0..15360} tokens
+    each take a 1,024-token chunk, Llama-3-8B-shaped, bf16."""
+    rng = np.random.default_rng(seed)
+    prefix = rng.integers(0, 15360, size=8, endpoint=True)
+    ctx = prefix + 1024
+    return make_prefill_case("prefill_chunked_llama3_8b", seed=seed, context_lens=ctx,
+                             query_lens=[1024] * 8, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, num_blocks=9000, max_blocks=1024,
+                             dtype=torch.bfloat16, rng=rng, fill=fill)
+
+
+def prefill_flops(case: PrefillCase) -> int:
+    """Useful flops: query i of n at position p = ctx - n + i scores p + 1
+    keys (2 D flops each) and sums as many values (2 D flops each), per query
+    head."""
+    total = 0
+    for c, n in zip(case.context_lens.tolist(), case.query_lens):
+        keys = n * (c - n) + n * (n + 1) // 2  # sum over the chunk of (p + 1)
+        total += 4 * case.head_dim * case.num_heads * keys
+    return total
+
+
+@dataclass
 class SwapPlan:
     """Preemption by swapping for one decode batch: the preempted sequences'
     blocks go to a CPU pool (swap-out) and, on resume, come back into free
@@ -306,4 +415,6 @@ CASES = {
     "parallel_sampling": lambda **kw: parallel_sampling(cow=False, **kw),
     "parallel_sampling_cow": lambda **kw: parallel_sampling(cow=True, **kw),
     "long_ctx": long_ctx,
+    "prefill_llama3_8b": prefill_llama3_8b,
+    "prefill_chunked_llama3_8b": prefill_chunked_llama3_8b,
 }

@@ -118,6 +118,40 @@ def test_python_swap_rejects_pageable_and_mismatched_pools():
         pa.pa_swap_blocks(k, v, k.clone(), v.clone(), m.int())
 
 
+def _prefill(lib, **kw):
+    args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, bt=ALIGNED, ctx=ALIGNED, qs=ALIGNED, scale=0.1,
+                out=ALIGNED, S=4, T=100, MQ=50, Hq=32, Hkv=8, D=128, B=16, MB=16, NB=100,
+                dtype=BF16, stream=None)
+    args.update(kw)
+    return lib.pa_prefill(args["q"], args["k"], args["v"], args["bt"], args["ctx"], args["qs"],
+                          args["scale"], args["out"], args["S"], args["T"], args["MQ"],
+                          args["Hq"], args["Hkv"], args["D"], args["B"], args["MB"], args["NB"],
+                          args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(MQ=101), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(qs=None), INVALID),
+    (dict(qs=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(B=32), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(S=70000), UNSUPPORTED),
+    (dict(T=10_000_000, MQ=10_000_000), UNSUPPORTED),
+    (dict(S=0), OK),
+    (dict(T=0, MQ=0), OK),
+])
+def test_prefill_argument_checks(kw, status):
+    lib = pa.load_library()
+    assert _prefill(lib, **kw) == status
+    if status != OK:
+        assert "pa_prefill" in lib.pa_last_error().decode()
+
+
 def test_workspace_size_query():
     lib = pa.load_library()
     # 32 seqs x 32 heads x ceil(4096/256) partitions x (128 + 2) floats

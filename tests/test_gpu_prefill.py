@@ -1,0 +1,193 @@
+"""GPU parity of pa_prefill (through its C ABI) against the oracle: the
+chunk's K/V go in with pa_write_kv, then every new query attends causally
+over its sequence's tokens in the pool."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_299_amd as pa
+from paged_kv_cache_299_amd import workloads
+
+from helpers import CODE, raw
+from parity import check_decode, log, same_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = torch.device("cuda:0")
+    pa.load_library()
+    return d
+
+
+def _case(ctxs, qlens, Hq, Hkv, D, dtype, seed=0, NB=None):
+    B = 16
+    need = sum(-(-c // B) for c in ctxs)
+    MB = max(1, max(-(-c // B) for c in ctxs))
+    return workloads.make_prefill_case("edge", seed=seed, context_lens=ctxs, query_lens=qlens,
+                                       num_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                                       num_blocks=need + 5 if NB is None else NB, max_blocks=MB,
+                                       dtype=dtype)
+
+
+def _x(dtype):
+    return 16 // torch.tensor([], dtype=dtype).element_size()
+
+
+def _oracle_pools(case):
+    """The pools after the chunk's write step, by the oracle."""
+    kc, vc = raw(case.k_cache), raw(case.v_cache)
+    st = case.write_step
+    if st is not None:
+        kc, vc = oracle.write_kv(raw(st.k_new), raw(st.v_new), kc, vc, st.slot_mapping.numpy(),
+                                 num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                                 block_size=case.block_size, k_x=_x(case.dtype),
+                                 dtype=CODE[case.dtype])
+    return kc, vc
+
+
+def _oracle_prefill(case, kc, vc, scale=None):
+    return oracle.prefill(raw(case.q), kc, vc, case.block_tables.numpy(),
+                          case.context_lens.numpy(), case.query_start.numpy(),
+                          case.scale if scale is None else scale,
+                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                          block_size=case.block_size, k_x=_x(case.dtype), dtype=CODE[case.dtype])
+
+
+class GpuPrefill:
+    def __init__(self, case, dev):
+        self.case = case
+        self.q = case.q.to(dev)
+        self.k = case.k_cache.to(dev)
+        self.v = case.v_cache.to(dev)
+        self.bt = case.block_tables.to(dev)
+        self.cl = case.context_lens.to(dev)
+        self.qs = case.query_start.to(dev)
+        self.out = torch.full_like(self.q, float("nan"))
+        st = case.write_step
+        if st is not None:
+            pa.pa_write_kv(st.k_new.to(dev), st.v_new.to(dev), self.k, self.v,
+                           st.slot_mapping.to(dev))
+
+    def run(self, scale=None, max_query_len=None):
+        pa.pa_prefill(self.q, self.k, self.v, self.bt, self.cl, self.qs,
+                      self.case.scale if scale is None else scale, self.out,
+                      max_query_len=max_query_len)
+        torch.cuda.synchronize()
+        return self.out.cpu()
+
+
+def _check(case, dev, label, scale=None, strict=False):
+    log(f"prefill {label}")
+    g = GpuPrefill(case, dev)
+    out = g.run(scale)
+    kc, vc = _oracle_pools(case)
+    assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc), f"{label}: pools differ"
+    ref = _oracle_prefill(case, kc, vc, scale)
+    check_decode(out, ref, case.dtype, label, strict=strict)
+    return g, out
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (8, 1), (16, 1), (32, 2), (3, 3),
+                                    (12, 4), (40, 1)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_edge_shapes(dev, dtype, Hq, Hkv, D):
+    """Whole prompts (lengths around block and tile edges), chunks after a
+    prefix, one query, no query."""
+    ctxs = [1, 15, 16, 17, 40, 200, 90, 33, 300]
+    qlens = [1, 15, 16, 17, 7, 200, 1, 0, 45]
+    case = _case(ctxs, qlens, Hq, Hkv, D, dtype, seed=Hq * 10 + D)
+    _check(case, dev, f"{dtype} Hq={Hq} Hkv={Hkv} D={D}")
+
+
+def test_many_workgroups_per_sequence_and_ragged_tails(dev):
+    """A 700-token prompt with 4 heads per kv head spans 22 workgroup row
+    tiles; the other sequences end inside tiles, waves and blocks."""
+    case = _case([700, 129, 513, 1000], [700, 129, 100, 999], 32, 8, 128, torch.bfloat16, seed=3)
+    _check(case, dev, "long prompts")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_negative_and_zero_scale(dev, scale):
+    case = _case([100, 37], [60, 37], 8, 2, 128, torch.bfloat16, seed=4)
+    _check(case, dev, f"scale {scale}", scale=scale)
+
+
+def test_physical_placement_does_not_change_gpu_output(dev):
+    case = _case([300, 77, 160], [300, 20, 1], 8, 2, 128, torch.bfloat16, seed=5, NB=64)
+    g = GpuPrefill(case, dev)
+    a = g.run()
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(64)).to(dev)
+    k2, v2 = torch.empty_like(g.k), torch.empty_like(g.v)
+    k2[perm] = g.k
+    v2[perm] = g.v
+    g.k, g.v = k2, v2
+    g.bt = perm[g.bt.long()].to(torch.int32)
+    b = g.run()
+    assert same_bits(a, b)
+
+
+def test_last_query_agrees_with_decode_within_tolerance(dev):
+    """n = 1 chunks: pa_prefill and pa_decode compute the same quantity (two
+    kernels, each within tolerance of the oracle's decode)."""
+    ctxs = [1, 100, 1000, 17]
+    case = _case(ctxs, [1] * 4, 32, 8, 128, torch.bfloat16, seed=6)
+    g, out = _check(case, dev, "single queries")
+    dec = torch.empty_like(g.q)
+    pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, dec)
+    torch.cuda.synchronize()
+    kc, vc = _oracle_pools(case)
+    ref = oracle.decode(raw(case.q), kc, vc, case.block_tables.numpy(), case.context_lens.numpy(),
+                        case.scale, num_kv_heads=8, head_dim=128, block_size=16, k_x=8,
+                        dtype=CODE[torch.bfloat16])
+    check_decode(dec.cpu(), ref, torch.bfloat16, "decode of the same tokens")
+
+
+def test_max_query_len_bound_larger_than_needed(dev):
+    """A loose host bound only adds empty workgroups."""
+    case = _case([50, 20], [50, 20], 8, 8, 64, torch.float16, seed=7)
+    g = GpuPrefill(case, dev)
+    a = g.run()
+    b = g.run(max_query_len=case.q.shape[0])
+    assert same_bits(a, b)
+
+
+def test_deterministic(dev):
+    case = _case([400, 90], [400, 30], 32, 8, 128, torch.bfloat16, seed=8)
+    g = GpuPrefill(case, dev)
+    assert same_bits(g.run(), g.run())
+
+
+@pytest.mark.parametrize("name", ["prefill_llama3_8b", "prefill_chunked_llama3_8b"])
+def test_workload_full_size_sampled_rows(dev, name):
+    """The benchmark workloads at full size, in the benchmark's launch
+    configuration.  The oracle computes sampled rows one by one: query i of
+    a chunk of n over ctx tokens is the decode of position p = ctx - n + i
+    over the first p + 1 tokens (a pinned identity of the oracle)."""
+    log(f"prefill full size {name}")
+    case = workloads.CASES[name]()
+    g = GpuPrefill(case, dev)
+    out = g.run(max_query_len=case.max_query_len)
+    assert torch.isfinite(out.to(torch.float32)).all()
+    kc, vc = _oracle_pools(case)
+    rng = np.random.default_rng(11)
+    qs = case.query_start.tolist()
+    rows, ctx_at, seq_of = [], [], []
+    for s, (c, n) in enumerate(zip(case.context_lens.tolist(), case.query_lens)):
+        picks = set(rng.choice(n, size=min(n, 6), replace=False).tolist()) | {0, n - 1}
+        for i in sorted(picks):
+            rows.append(qs[s] + i)
+            ctx_at.append(c - n + i + 1)
+            seq_of.append(s)
+    q_rows = case.q[rows]
+    ref = oracle.decode(raw(q_rows), kc, vc, case.block_tables.numpy()[seq_of],
+                        np.array(ctx_at, np.int32), case.scale, num_kv_heads=case.num_kv_heads,
+                        head_dim=case.head_dim, block_size=case.block_size, k_x=_x(case.dtype),
+                        dtype=CODE[case.dtype])
+    # early queries of a prompt average few values: their outputs sit near
+    # +-2, where the bf16 output's own rounding alone exceeds 2e-3, so the
+    # bound is 2e-3 beyond that rounding, as for every other prefill case
+    check_decode(out[rows], ref, case.dtype, f"{name} ({len(rows)} sampled rows)")
