@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions (0 = skip)")
     ap.add_argument("--seed", type=int, default=None,
                     help="draw of the workload (default: the workload's own seed)")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode with pa_decode_cascade: shared prefix blocks read once per "
+                         "group of sequences (groups from the block tables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's plain copy of a 1 GiB tensor (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale)")
@@ -120,6 +123,18 @@ def measured_traffic(workload, part, root=ROOT):
             if hashlib.sha256(f.read()).hexdigest() != digest:
                 return None, rel
     return int(rec["bytes_per_launch"]), rel
+
+
+def unique_decode_bytes(block_tables, ctx, S, Hq, Hkv, D, B, e):
+    """decode_bytes with each physical block's tokens counted once, however
+    many sequences read it: the HBM lower bound when blocks are shared."""
+    used = {}
+    for s in range(S):
+        for i in range(-(-ctx[s] // B)):
+            phys = int(block_tables[s, i])
+            used[phys] = max(used.get(phys, 0), min(B, ctx[s] - i * B))
+    kv = 2 * sum(used.values()) * Hkv * D * e
+    return kv + 2 * S * Hq * D * e + 4 * sum(-(-c // B) for c in ctx) + 4 * S
 
 
 def decode_bytes(ctx, S, Hq, Hkv, D, B, e):
@@ -193,7 +208,10 @@ def main():
     ctx = case.context_lens.tolist()
     # the hint a serving system gives from its block reference counts
     shared = workloads.shares_blocks(case.block_tables, case.context_lens, B)
+    gs, pb, max_group = workloads.shared_prefix_groups(case.block_tables, case.context_lens, B)
+    gs_d, pb_d = gs.to(dev), pb.to(dev)
     dec_bytes = decode_bytes(ctx, S, Hq, Hkv, D, B, e)
+    uniq_bytes = unique_decode_bytes(case.block_tables, ctx, S, Hq, Hkv, D, B, e)
     step_bytes = dec_bytes
     for st in case.steps:
         if isinstance(st, workloads.CopyStep):
@@ -213,7 +231,10 @@ def main():
                     pa.pa_copy_blocks(k, v, st[1])
                 else:
                     pa.pa_write_kv(st[1], st[2], k, v, st[3])
-        if decode:
+        if decode and args.cascade:
+            pa.pa_decode_cascade(q, k, v, bt, cl, gs_d, pb_d, case.scale, out,
+                                 max_group_size=max_group, partition_tokens=part)
+        elif decode:
             pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part,
                          shared_blocks=shared)
 
@@ -267,8 +288,10 @@ def main():
     dec_avg = dec_ms / args.steps
     wr_avg = wr_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
-    traffic, traffic_src = measured_traffic(args.workload, part)
+    # roofline bytes: each physical block counted once (equal to dec_bytes
+    # unless blocks are shared; then the logical rate is reported as effective)
+    achieved = uniq_bytes / (dec_avg * 1e-3) / 1e9
+    traffic, traffic_src = (None, None) if args.cascade else measured_traffic(args.workload, part)
 
     # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
     cpu = None
@@ -313,19 +336,25 @@ def main():
                    "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
                    "seed": case.seed, "partition_tokens": part or "auto",
-                   "shared_blocks_hint": shared,
+                   "shared_blocks_hint": shared, "cascade": bool(args.cascade),
+                   "groups": int(pb.shape[0]), "max_group_size": int(max_group),
                    "layers_rotated": args.layers},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),
         "decode_us": round(dec_avg * 1e3, 2),
+        "decode_entry": "pa_decode_cascade" if args.cascade else "pa_decode",
+        "logical_bytes": int(dec_bytes),
+        "unique_bytes": int(uniq_bytes),
         "write_us": round(wr_avg * 1e3, 2),
         "launch": "HIP graph replays, one graph per pass over the rotated layers",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "pa_decode (partition + merge kernels)",
-                     "bytes_per_launch": int(dec_bytes)},
+                     "kernel": ("pa_decode_cascade (unit + merge kernels)" if args.cascade
+                                else "pa_decode (partition + merge kernels)"),
+                     "bytes_per_launch": int(uniq_bytes)},
+        "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

@@ -144,6 +144,45 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int partition_tokens, int flags, void *stream);
 
 /*
+ * pa_decode_cascade -- pa_decode for sequences that share prefix blocks,
+ * reading each shared block once per group instead of once per sequence.
+ * Under parallel sampling (or beam search) the samples of one prompt keep
+ * the prompt's blocks physically shared through copy-on-write.
+ *   [論文解説: PagedAttention, 技術的詳細 › Copy-on-Write KVキャッシュ共有]
+ *
+ * Arguments as pa_decode, plus:
+ *   group_start     int32 [num_groups + 1], device: group i is sequences
+ *                   group_start[i] .. group_start[i+1]-1 (consecutive),
+ *                   group_start[0] = 0, group_start[num_groups] = num_seqs
+ *                   (a sequence that shares nothing is a group of one)
+ *   prefix_blocks   int32 [num_groups], device: the first prefix_blocks[i]
+ *                   block-table entries are the same physical blocks in every
+ *                   member of group i, and every member's context covers them
+ *                   (prefix_blocks[i] * 16 <= context_lens[s]); 0 = nothing
+ *                   shared
+ *   max_group_size  host bound on the members of a group (sizes the launch)
+ *   partition_tokens  0 (256) or a multiple of 16 in [16, 1024]: shared
+ *                   prefixes and private suffixes are cut into runs of at
+ *                   most that many tokens
+ * The result is the attention pa_decode computes, up to rounding: the shared
+ * keys are scored against the queries of every member of the group at once
+ * (one read of each shared block per group and kv head), each sequence's own
+ * keys against its own queries, and the partial results are merged with
+ * log-sum-exp weights (the streaming softmax is associative).
+ * bf16 and fp16; fp32 is PA_ERR_UNSUPPORTED.  Uses the same per-stream
+ * workspace as pa_decode: num_seqs * num_heads * 2 * ceil(max_blocks_per_seq
+ * * 16 / P) * (head_dim + 2) floats.
+ * Errors: as pa_decode; PA_ERR_INVALID_ARG also when groups cannot cover the
+ * sequences (num_groups > num_seqs, max_group_size outside [1, num_seqs]).
+ */
+int pa_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      const int32_t *group_start, const int32_t *prefix_blocks, int num_groups,
+                      int max_group_size, float scale, void *out, int num_seqs, int num_heads,
+                      int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                      int64_t num_blocks, int dtype, int partition_tokens, void *stream);
+
+/*
  * pa_prefill -- paged prefill attention: the queries of a chunk of new tokens
  * attend causally over their sequence's tokens in the pool.  The same block
  * gather as decode serves the prefill phase.

@@ -10,6 +10,8 @@ Shapes (see layout.py for the pool format):
   pa_decode(q [S,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
     (calls pa_decode_ex; shared_blocks sets the PA_DECODE_SHARED_BLOCKS hint)
+  pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, group_start int32 [NG+1],
+                    prefix_blocks int32 [NG], scale, out, max_group_size=None)
   pa_prefill(q [T,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
              query_start int32 [S+1], scale, out [T,Hq,D], max_query_len=None)
   pa_copy_blocks(k_cache, v_cache, block_mapping int64 [n,2])
@@ -35,7 +37,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_prefill", "pa_copy_blocks", "pa_swap_blocks",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_cascade", "pa_prefill",
+    "pa_copy_blocks", "pa_swap_blocks",
     "pa_status_str",
     "pa_last_error", "pa_decode_workspace_bytes", "pa_release_workspaces", "pa_version",
 )
@@ -72,6 +75,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
+    lib.pa_decode_cascade.argtypes = [P, P, P, P, P, P, P, I32, I32, F32, P, I32, I32, I32, I32,
+                                      I32, I32, I64, I32, I32, P]
+    lib.pa_decode_cascade.restype = I32
     lib.pa_prefill.argtypes = [P, P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I32, I32,
                                I64, I32, P]
     lib.pa_prefill.restype = I32
@@ -180,6 +186,43 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_decode_cascade(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      group_start: torch.Tensor, prefix_blocks: torch.Tensor, scale: float,
+                      out: torch.Tensor, max_group_size: Optional[int] = None,
+                      partition_tokens: int = 0, stream=None) -> None:
+    """pa_decode with the first prefix_blocks[i] blocks of the sequences of
+    group i (group_start[i] .. group_start[i+1]-1) read once for the group.
+    max_group_size: a bound on the members of a group; None reads it from
+    group_start (a device-to-host copy)."""
+    NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
+    S, Hq = q.shape[0], q.shape[1]
+    _need(q.dim() == 3 and q.shape[2] == D and q.shape == out.shape,
+          "q and out must be [S, Hq, D] with the caches' D")
+    _need(q.dtype == k_cache.dtype == out.dtype, "q, caches and out differ in dtype")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S and block_tables.is_contiguous(),
+          "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,)
+          and context_lens.is_contiguous(), "context_lens must be contiguous int32 [S]")
+    NG = prefix_blocks.shape[0]
+    _need(group_start.dtype == torch.int32 and tuple(group_start.shape) == (NG + 1,)
+          and group_start.is_contiguous(), "group_start must be contiguous int32 [NG + 1]")
+    _need(prefix_blocks.dtype == torch.int32 and prefix_blocks.dim() == 1
+          and prefix_blocks.is_contiguous(), "prefix_blocks must be contiguous int32 [NG]")
+    for t in (q, out, block_tables, context_lens, group_start, prefix_blocks):
+        _need(t.device == k_cache.device, "all tensors must be on the caches' GPU")
+    if max_group_size is None:
+        max_group_size = int((group_start[1:] - group_start[:-1]).max().item()) if NG else 0
+    rc = load_library().pa_decode_cascade(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(group_start), _ptr(prefix_blocks), NG, int(max_group_size), float(scale), _ptr(out),
+        S, Hq, Hkv, D, B, block_tables.shape[1], NB, DTYPE_CODES[q.dtype], int(partition_tokens),
+        _stream_handle(stream, k_cache.device))
+    _check(rc, "pa_decode_cascade")
 
 
 def pa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -374,6 +374,101 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
                         num_blocks, dtype, 0, 0, stream);
 }
 
+int pa_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      const int32_t *group_start, const int32_t *prefix_blocks, int num_groups,
+                      int max_group_size, float scale, void *out, int num_seqs, int num_heads,
+                      int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                      int64_t num_blocks, int dtype, int partition_tokens, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode_cascade: unknown dtype %d", dtype);
+    if (num_seqs < 0 || num_groups < 0 || max_group_size < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_cascade: sizes must be positive");
+    if (num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_cascade: num_heads %d is not a multiple of %d", num_heads,
+                    num_kv_heads);
+    if (!isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_cascade: scale is not finite");
+    if ((num_seqs > 0) != (num_groups > 0) || num_groups > num_seqs ||
+        (num_seqs > 0 && (max_group_size < 1 || max_group_size > num_seqs)))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_cascade: %d groups of at most %d sequences "
+                    "cannot cover %d sequences", num_groups, max_group_size, num_seqs);
+    if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % kBlock != 0 ||
+                                                          partition_tokens > kMaxPartition)))
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_cascade: partition_tokens %d must be 0 or a multiple of 16 in "
+                    "[16, %d]", partition_tokens, kMaxPartition);
+    if (dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: fp32 (the matrix-core path takes "
+                    "16-bit data)");
+    if (block_size != kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: block_size %d (only 16 is built)",
+                    block_size);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: head_dim %d (64 and 128 are built)",
+                    head_dim);
+    if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: max_blocks_per_seq too large");
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !group_start ||
+        !prefix_blocks || !out)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_cascade: null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+        ((uintptr_t)group_start & 3u) || ((uintptr_t)prefix_blocks & 3u))
+        return fail(PA_ERR_INVALID_ARG,
+                    "pa_decode_cascade: data pointers must be 16-byte aligned");
+
+    const int G = num_heads / num_kv_heads;
+    const int P = partition_tokens > 0 ? partition_tokens : 256;
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * kBlock;
+    const int64_t np = max_tokens > 0 ? (max_tokens + P - 1) / P : 1;
+    const int64_t tiles = ((int64_t)max_group_size * G + 15) / 16;
+    // units: prefix (group, partition, tile, kv head) + suffix (sequence, partition, kv head)
+    const int64_t units = ((int64_t)num_groups * tiles + num_seqs) * np * num_kv_heads;
+    if (units > (int64_t)0x7fffffff - 65536 || (int64_t)num_seqs * num_heads > 0x7fffffff / 64)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_cascade: %lld work units",
+                    (long long)units);
+    // the workgroups walk the unit list; one wave each, a few per SIMD
+    const int grid = (int)(units < 4096 ? (units > 0 ? units : 1) : 4096);
+
+    pa::CascadeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.bt = block_tables;
+    a.ctx = context_lens;
+    a.gs = group_start;
+    a.pblk = prefix_blocks;
+    a.out = out;
+    a.scale_log2_abs = fabsf(scale) * 1.4426950408889634f;
+    a.q_xor = scale < 0.f ? (int)0x80008000u : 0;
+    a.S = num_seqs;
+    a.NG = num_groups;
+    a.Hq = num_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.MB = max_blocks_per_seq;
+    a.P = P;
+    a.NPP = (int)np;
+    a.NPT = (int)(2 * np);
+    a.NB = num_blocks;
+    void *ws = nullptr;
+    const size_t rows = (size_t)num_seqs * num_heads;
+    const size_t o_bytes = rows * a.NPT * head_dim * sizeof(float);
+    const size_t ml_bytes = rows * a.NPT * 2 * sizeof(float);
+    int rc = workspace_for((hipStream_t)stream, o_bytes + ml_bytes, &ws);
+    if (rc != PA_OK) return rc;
+    a.part_o = (float *)ws;
+    a.part_ml = (float *)((char *)ws + o_bytes);
+    hipError_t err = pa::launch_cascade(a, dtype, head_dim, grid, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "pa_decode_cascade launch");
+    return PA_OK;
+}
+
 int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
                const int32_t *block_tables, const int32_t *context_lens,
                const int32_t *query_start, float scale, void *out, int num_seqs, int num_tokens,

@@ -199,4 +199,35 @@ __device__ __forceinline__ void issue_point() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// D = A . B + C on v_mfma_f32_16x16x16: lane l supplies A[l % 16][4 (l / 16) .. +4]
+// and B[4 (l / 16) .. +4][l % 16] and receives D[4 (l / 16) .. +4][l % 16].
+template <int DT> __device__ __forceinline__ f32x4 mfma16(const i32x2 &a, const i32x2 &b, const f32x4 &c) {
+    if constexpr (DT == kBF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                         __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+}
+
+// Clamp a context length read from the device to what the block table holds.
+__device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+// ---------------------------------------------------------------------------
+// A context of ctx tokens is cut into the fewest partitions of at most P
+// tokens, ceil(ctx / P), all of the same number of whole blocks except a
+// shorter last one (a 1100-token context at P = 1024 gives 2 x 35 blocks, not
+// 64 + 5): the partitions of a sequence then take about the same time, and
+// fewer units run at the full length P.  Returns the blocks per partition;
+// every partition holds at least one token (ceil(nb / ceil(nb / n)) = n for
+// n = ceil(nb / PB), the partition count the units are counted with).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int blocks_per_partition(int ctx, int P) {
+    const int nb = (ctx + kB - 1) / kB;
+    if (ctx <= P) return nb;
+    const int n = (ctx + P - 1) / P;
+    return (nb + n - 1) / n;
+}
+
 }  // namespace pa

@@ -52,6 +52,29 @@ int64_t prefill_row_tiles(int64_t max_query_len, int G);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int max_query_len,
                           hipStream_t stream);
 
+// Decode with shared prefixes (16-bit data, B = 16).
+struct CascadeArgs {
+    const void *q;          // [S][Hq][D]
+    const void *k;          // K pool
+    const void *v;          // V pool
+    const int *bt;          // [S][MB]
+    const int *ctx;         // [S]
+    const int *gs;          // [NG+1] first sequence of each group
+    const int *pblk;        // [NG] shared blocks of each group
+    void *out;              // [S][Hq][D]
+    float *part_o;          // [S][Hq][NPT][D]
+    float *part_ml;         // [S][Hq][NPT][2]
+    float scale_log2_abs;
+    int q_xor;
+    int S, NG, Hq, Hkv, G, MB, P;
+    int NPP;                // partial slots per row for the prefix (ceil(MB * 16 / P))
+    int NPT;                // partial slots per row in all (prefix + suffix)
+    int64_t NB;
+};
+
+hipError_t launch_cascade(const CascadeArgs &a, int dtype, int head_dim, int grid,
+                          hipStream_t stream);
+
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
                            int elem_bytes, hipStream_t stream);

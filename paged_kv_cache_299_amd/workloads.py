@@ -193,7 +193,8 @@ def long_ctx(seed: int = 5, fill: bool = True) -> DecodeCase:
 def parallel_sampling(seed: int = 4, cow: bool = False, num_prompts: int = 16,
                       samples: int = 8, prompt_tokens: Optional[int] = None,
                       max_private: int = 256, num_heads: int = 32, head_dim: int = 128,
-                      num_blocks: int = 4096, fill: bool = True) -> DecodeCase:
+                      num_blocks: int = 4096, fill: bool = True,
+                      num_kv_heads: Optional[int] = None) -> DecodeCase:
     """Parallel sampling over shared prompt blocks.
 
     Sequence id = prompt * samples + sample.  Sample 0 holds the prompt, the
@@ -214,7 +215,7 @@ def parallel_sampling(seed: int = 4, cow: bool = False, num_prompts: int = 16,
     P = (1016 if cow else 1024) if prompt_tokens is None else prompt_tokens
     S = num_prompts * samples
     n_priv = rng.integers(1 if cow else 0, max_private, size=S, endpoint=True)
-    Hkv = num_heads
+    Hkv = num_heads if num_kv_heads is None else num_kv_heads
     max_blocks = -(-(P + max_private) // B)
     bm = BlockManager(num_blocks, B, free_order=rng.permutation(num_blocks))
     for p in range(num_prompts):
@@ -406,6 +407,34 @@ def swap_plan(case: DecodeCase, num_preempted: int, seed: int = 7) -> SwapPlan:
     out_map = torch.from_numpy(np.stack([np.array(dev_blocks, dtype=np.int64), host], 1))
     in_map = torch.from_numpy(np.stack([host, back], 1))
     return SwapPlan(order, out_map.contiguous(), in_map.contiguous(), n)
+
+
+def shared_prefix_groups(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         block_size: int) -> Tuple[torch.Tensor, torch.Tensor, int]:
+    """Groups of consecutive sequences whose tables start with the same
+    physical block, and per group the number of leading table entries that
+    are the same block in every member and lie wholly inside every member's
+    context.  Returns (group_start int32 [NG+1], prefix_blocks int32 [NG],
+    largest group size); a sequence that shares nothing is a group of one."""
+    bt = block_tables.numpy()
+    ctx = [int(c) for c in context_lens.tolist()]
+    S = len(ctx)
+    starts, prefix = [0], []
+    s = 0
+    while s < S:
+        e = s + 1
+        while e < S and ctx[s] > 0 and ctx[e] > 0 and bt[e, 0] == bt[s, 0]:
+            e += 1
+        full = min(ctx[s:e]) // block_size
+        n = 0
+        while n < full and all(bt[t, n] == bt[s, n] for t in range(s + 1, e)):
+            n += 1
+        prefix.append(n if e - s > 1 else 0)
+        starts.append(e)
+        s = e
+    sizes = [starts[i + 1] - starts[i] for i in range(len(prefix))]
+    return (torch.tensor(starts, dtype=torch.int32), torch.tensor(prefix, dtype=torch.int32),
+            max(sizes, default=0))
 
 
 CASES = {

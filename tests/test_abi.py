@@ -152,6 +152,41 @@ def test_prefill_argument_checks(kw, status):
         assert "pa_prefill" in lib.pa_last_error().decode()
 
 
+def _cascade(lib, **kw):
+    args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, bt=ALIGNED, ctx=ALIGNED, gs=ALIGNED, pb=ALIGNED,
+                NG=2, MG=4, scale=0.1, out=ALIGNED, S=8, Hq=32, Hkv=8, D=128, B=16, MB=16,
+                NB=100, dtype=BF16, P=0, stream=None)
+    args.update(kw)
+    return lib.pa_decode_cascade(args["q"], args["k"], args["v"], args["bt"], args["ctx"],
+                                 args["gs"], args["pb"], args["NG"], args["MG"], args["scale"],
+                                 args["out"], args["S"], args["Hq"], args["Hkv"], args["D"],
+                                 args["B"], args["MB"], args["NB"], args["dtype"], args["P"],
+                                 args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(NG=9), INVALID),
+    (dict(NG=0), INVALID),
+    (dict(MG=0), INVALID),
+    (dict(MG=9), INVALID),
+    (dict(P=24), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(gs=None), INVALID),
+    (dict(pb=ctypes.c_void_p((1 << 20) + 2)), INVALID),
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(B=8), UNSUPPORTED),
+    (dict(D=80), UNSUPPORTED),
+    (dict(S=0, NG=0, MG=0), OK),
+])
+def test_cascade_argument_checks(kw, status):
+    lib = pa.load_library()
+    assert _cascade(lib, **kw) == status
+    if status != OK:
+        assert "pa_decode_cascade" in lib.pa_last_error().decode()
+
+
 def test_workspace_size_query():
     lib = pa.load_library()
     # 32 seqs x 32 heads x ceil(4096/256) partitions x (128 + 2) floats
