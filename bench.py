@@ -50,6 +50,10 @@ WORKLOAD_TEXT = {
     "prefill_chunked_llama3_8b": "chunked paged prefill, one layer: 8 sequences with cached "
                                  "prefixes of U{0..15360} tokens take 1,024-token chunks, "
                                  "32 q / 8 kv heads, D 128, B 16, bf16",
+    "vattention_llama3_8b": "the Llama-3-8B-shaped decode batch (32 seqs, 32 q / 8 kv heads, "
+                            "D 128, bf16) on virtual-memory KV storage: one contiguous range "
+                            "per request slot (max context 4096), pages mapped on demand, "
+                            "decode without a block table",
     "swap_llama3_8b": "preemption by swapping, one layer: the 8 longest sequences of the "
                       "Llama-3-8B-shaped batch (1,744 blocks of 8 kv heads x 16 tokens x D 128, "
                       "bf16) out to pinned host memory and back into other free device blocks",
@@ -73,6 +77,8 @@ def parse():
     ap.add_argument("--cascade", action="store_true",
                     help="decode with pa_decode_cascade: shared prefix blocks read once per "
                          "group of sequences (groups from the block tables)")
+    ap.add_argument("--page-kib", type=int, default=2048,
+                    help="page size of the virtual-memory KV storage (vattention workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's plain copy of a 1 GiB tensor (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale)")
@@ -174,6 +180,9 @@ def main():
         return
     if args.workload.startswith("prefill_"):
         bench_prefill(args, dev)
+        return
+    if args.workload.startswith("vattention_"):
+        bench_vattention(args, dev)
         return
 
     t_setup = time.time()
@@ -526,6 +535,166 @@ def bench_prefill(args, dev):
                      "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "pa_prefill (prefill_mfma_kernel)",
                      "flops_per_launch": int(flops)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_vattention(args, dev):
+    """The Llama-3-8B-shaped decode batch stored twice per rotated layer: on
+    virtual-memory storage (VirtualKV: request slot s = sequence s, pages
+    mapped for its context) and in the paged pool with the workload's block
+    tables.  Both decodes run as graph replays over the layers; the paging
+    overhead is paged time / table-free time - 1."""
+    import torch
+
+    import paged_kv_cache_299_amd as pa
+    from paged_kv_cache_299_amd import workloads
+    from paged_kv_cache_299_amd.layout import kv_cache_shapes
+
+    t_setup = time.time()
+    case = workloads.llama3_8b(fill=False, **({} if args.seed is None else {"seed": args.seed}))
+    S, Hq, Hkv, D, B, NB, dt = case.num_seqs, case.num_heads, case.num_kv_heads, \
+        case.head_dim, case.block_size, case.num_blocks, case.dtype
+    e = 2
+    ctx = case.context_lens.tolist()
+    max_ctx = case.max_blocks * B
+    L = args.layers
+    vkv = pa.VirtualKV(L, S, max_ctx, Hkv, D, dt, page_bytes=args.page_kib * 1024)  # 0 = the library default
+    reqs = [vkv.alloc_reqid() for _ in range(S)]
+    lens = [0] * S
+    for r, c in zip(reqs, ctx):
+        lens[r] = c
+    t0 = time.perf_counter()
+    vkv.step(lens)
+    step_ms = (time.perf_counter() - t0) * 1e3
+    info = vkv.info()
+    # the same tokens in both layouts
+    T = int(sum(ctx))
+    vslots = torch.tensor([vkv.slot(r, i) for r, c in zip(reqs, ctx) for i in range(c)],
+                          dtype=torch.int64, device=dev)
+    bt_np = case.block_tables.numpy()
+    pslots = torch.tensor([int(bt_np[s, i // B]) * B + i % B for s in range(S)
+                           for i in range(ctx[s])], dtype=torch.int64, device=dev)
+    k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
+    gen = torch.Generator(device=dev)
+    pools = []
+    for layer in range(L):
+        gen.manual_seed(4000 + layer)
+        kn = torch.randn((T, Hkv, D), generator=gen, device=dev).to(dt)
+        vn = torch.randn((T, Hkv, D), generator=gen, device=dev).to(dt)
+        vkv.write_kv(layer, kn, vn, vslots)
+        kp = torch.empty(k_shape, dtype=dt, device=dev)
+        vp = torch.empty(v_shape, dtype=dt, device=dev)
+        pa.pa_write_kv(kn, vn, kp, vp, pslots)
+        pools.append((kp, vp))
+        del kn, vn
+    q = case.q.to(dev)
+    req_d = torch.tensor(reqs, dtype=torch.int32, device=dev)
+    bt = case.block_tables.to(dev)
+    cl = case.context_lens.to(dev)
+    out_v = torch.empty_like(q)
+    out_p = torch.empty_like(q)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    stream = torch.cuda.Stream()
+
+    def enqueue(layer, paged):
+        if paged:
+            kp, vp = pools[layer]
+            pa.pa_decode(q, kp, vp, bt, cl, case.scale, out_p)
+        else:
+            vkv.decode(layer, q, req_d, cl, case.scale, out_v)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            enqueue(i % L, False)
+            enqueue(i % L, True)
+    torch.cuda.synchronize()
+
+    def timed(n, paged):
+        q_, r_ = divmod(n, L)
+        graphs = []
+        for layers in ([range(L)] * (1 if q_ else 0)) + ([range(r_)] if r_ else []):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for l in layers:
+                    enqueue(l, paged)
+            graphs.append(g)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(q_):
+                graphs[0].replay()
+            if r_:
+                graphs[-1].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return wall, e0.elapsed_time(e1)
+
+    wall, v_ms = timed(args.steps, paged=False)
+    _, p_ms = timed(args.steps, paged=True)
+    v_avg, p_avg = v_ms / args.steps, p_ms / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    dec_bytes = decode_bytes(ctx, S, Hq, Hkv, D, B, e) - 4 * sum(-(-c // B) for c in ctx)
+    identical = bool(torch.equal(out_v.view(torch.int16), out_p.view(torch.int16)))
+    achieved = dec_bytes / (v_avg * 1e-3) / 1e9
+    vkv.close()
+
+    cpu = None
+    if args.cpu_reps > 0:
+        import oracle
+        kp, vp = pools[0]
+        kh, vh = raw_bits(kp.cpu()), raw_bits(vp.cpu())
+        times = []
+        for _ in range(args.cpu_reps):
+            t = time.perf_counter()
+            oracle.decode(raw_bits(case.q), kh, vh, case.block_tables.numpy(),
+                          case.context_lens.numpy(), case.scale, num_kv_heads=Hkv, head_dim=D,
+                          block_size=B, k_x=8, dtype=pa.DTYPE_CODES[dt])
+            times.append(time.perf_counter() - t)
+        t_med = statistics.median(times)
+        cpu = {"value": round(dec_bytes / t_med / 1e9, 3), "unit": "GB/s",
+               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"the full batch (all {S} sequences, layer 0's tokens), median of "
+                         f"{args.cpu_reps} runs, fp64"}
+
+    rec = {
+        "metric": "decode attention on virtual-memory KV storage (no block table): achieved "
+                  "HBM GB/s at 1 GPU",
+        "value": round(dec_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q, the Llama-3-8B-shaped batch's lengths)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+                   "num_seqs": S, "context_tokens": T, "max_context_len": max_ctx,
+                   "page_bytes": info["page_bytes"], "layers_rotated": L, "seed": case.seed},
+        "vkv_decode_us": round(v_avg * 1e3, 2),
+        "paged_decode_us": round(p_avg * 1e3, 2),
+        "paging_overhead_pct": round(100 * (p_avg / v_avg - 1), 2),
+        "outputs_bit_identical": identical,
+        "mapped_bytes": info["mapped_bytes"],
+        "step_map_ms": round(step_ms, 2),
+        "create_us_per_page": round(info["create_us_per_page"], 2),
+        "map_us_per_page": round(info["map_us_per_page"], 2),
+        "launch": "HIP graph replays, one graph per pass over the rotated layers",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "pa_vkv_decode (partition + merge kernels, no block table)",
+                     "bytes_per_launch": int(dec_bytes)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

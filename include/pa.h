@@ -267,6 +267,84 @@ int pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_
                    int head_dim, int block_size, int64_t num_src_blocks, int64_t num_dst_blocks,
                    int dtype, void *stream);
 
+/*
+ * ---- KV storage on virtual memory (the vAttention design) -----------------
+ * Virtual address space is reserved up front for every (layer, K/V) buffer:
+ * max_batch request slots of max_context_len tokens each, contiguous per
+ * slot.  Physical pages are created and mapped into a slot's range only when
+ * its sequence grows (pa_vkv_step), and stay mapped after the request ends
+ * until pa_vkv_reclaim (deferred reclamation), so a new request on that slot
+ * reuses them.  Decode and writes then address a sequence's tokens by
+ * arithmetic (slot r, position i), with no block table.
+ *   [論文解説: vAttention, 技術的詳細 › CUDA Virtual Memory Management APIの
+ *    活用; 仮想メモリの事前予約; リクエスト単位のKVキャッシュインデキシング;
+ *    Demand Paging vs Pre-allocation; 実装のポイント (init / alloc_reqid /
+ *    step / free_reqid)]
+ *
+ * Inside a slot's range tokens keep the library's storage format: position
+ * i of slot r is in block r * request_stride_blocks + i / 16 of the K and V
+ * pools of pa_vkv_layer, at offset i % 16 (the pools described above, with
+ * num_blocks = max_batch * request_stride_blocks and B = 16).
+ * All calls are host calls on the device current at pa_vkv_create; a pa_vkv
+ * is not thread-safe.  Mapping is synchronous (pa_vkv_step returns when the
+ * new pages are usable); pa_vkv_reclaim and pa_vkv_destroy synchronize the
+ * device before unmapping.  Reading a position that no page backs would be a
+ * memory fault: pa_vkv_write_kv skips, and pa_vkv_decode clamps each context
+ * to, the tokens mapped for the slot.
+ */
+typedef struct pa_vkv pa_vkv;
+
+/* Reserve the virtual ranges.  page_bytes 0 = the device's recommended
+ * allocation granularity (hipMemGetAllocationGranularity) doubled up to at
+ * least 2 MiB, else a multiple of the minimum granularity.
+ * max_context_len a multiple of 16.  Errors: PA_ERR_INVALID_ARG (sizes,
+ * dtype, page size), PA_ERR_UNSUPPORTED (no virtual memory management on the
+ * device, or pages and 16-token blocks that do not tile a slot), PA_ERR_HIP. */
+int pa_vkv_create(int num_layers, int max_batch, int max_context_len, int num_kv_heads,
+                  int head_dim, int dtype, int64_t page_bytes, pa_vkv **out);
+
+/* Sizes and counters (each output pointer may be NULL): the page size, the
+ * slot stride in 16-token blocks, the bytes currently mapped over all
+ * buffers, and the mean host time of hipMemCreate and of hipMemMap +
+ * hipMemSetAccess per page so far. */
+int pa_vkv_info(const pa_vkv *v, int64_t *page_bytes, int64_t *request_stride_blocks,
+                int64_t *mapped_bytes, double *create_us_per_page, double *map_us_per_page);
+
+/* Base addresses of layer `layer`'s K and V pools (device virtual addresses). */
+int pa_vkv_layer(const pa_vkv *v, int layer, void **k_cache, void **v_cache);
+
+/* Take a free slot, preferring one whose pages are still mapped.
+ * PA_ERR_NO_MEMORY when every slot is in use. */
+int pa_vkv_alloc_reqid(pa_vkv *v, int *req_id);
+
+/* Map pages so that slot r holds seq_lens[r] tokens (host int32
+ * [max_batch]) in every layer.  Never unmaps.  PA_ERR_NO_MEMORY when the
+ * device runs out of memory (pages mapped before the failure stay). */
+int pa_vkv_step(pa_vkv *v, const int32_t *seq_lens);
+
+/* Release a slot; its pages stay mapped until pa_vkv_reclaim. */
+int pa_vkv_free_reqid(pa_vkv *v, int req_id);
+
+/* Unmap and release the pages of every free slot (synchronizes the device). */
+int pa_vkv_reclaim(pa_vkv *v);
+
+/* Synchronize the device, unmap everything and free the reservations. */
+int pa_vkv_destroy(pa_vkv *v);
+
+/* pa_write_kv into layer `layer`: slot = r * request_stride_blocks * 16 + i
+ * for position i of slot r (int64, device); slots < 0 and positions without
+ * a mapped page are skipped. */
+int pa_vkv_write_kv(const pa_vkv *v, int layer, const void *k_new, const void *v_new,
+                    const int64_t *slot_mapping, int64_t num_tokens, void *stream);
+
+/* pa_decode over layer `layer` without a block table: sequence s reads slot
+ * req_ids[s] (int32 [num_seqs], device), positions 0 .. context_lens[s]-1.
+ * Same arithmetic and kernels as pa_decode; q / out as there.
+ * partition_tokens as pa_decode_ex (0 = automatic). */
+int pa_vkv_decode(const pa_vkv *v, int layer, const void *q, const int32_t *req_ids,
+                  const int32_t *context_lens, float scale, void *out, int num_seqs,
+                  int num_heads, int partition_tokens, void *stream);
+
 /* Name of a status code (static string, never NULL). */
 const char *pa_status_str(int status);
 

@@ -39,6 +39,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 EXPORTS = (
     "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_cascade", "pa_prefill",
     "pa_copy_blocks", "pa_swap_blocks",
+    "pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid", "pa_vkv_step",
+    "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy", "pa_vkv_write_kv", "pa_vkv_decode",
     "pa_status_str",
     "pa_last_error", "pa_decode_workspace_bytes", "pa_release_workspaces", "pa_version",
 )
@@ -75,6 +77,21 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
+    PP, PI64, PD = ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double)
+    lib.pa_vkv_create.argtypes = [I32, I32, I32, I32, I32, I32, I64, PP]
+    lib.pa_vkv_info.argtypes = [P, PI64, PI64, PI64, PD, PD]
+    lib.pa_vkv_layer.argtypes = [P, I32, PP, PP]
+    lib.pa_vkv_alloc_reqid.argtypes = [P, ctypes.POINTER(I32)]
+    lib.pa_vkv_step.argtypes = [P, P]
+    lib.pa_vkv_free_reqid.argtypes = [P, I32]
+    lib.pa_vkv_reclaim.argtypes = [P]
+    lib.pa_vkv_destroy.argtypes = [P]
+    lib.pa_vkv_write_kv.argtypes = [P, I32, P, P, P, I64, P]
+    lib.pa_vkv_decode.argtypes = [P, I32, P, P, P, F32, P, I32, I32, I32, P]
+    for name in ("pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid",
+                 "pa_vkv_step", "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy",
+                 "pa_vkv_write_kv", "pa_vkv_decode"):
+        getattr(lib, name).restype = I32
     lib.pa_decode_cascade.argtypes = [P, P, P, P, P, P, P, I32, I32, F32, P, I32, I32, I32, I32,
                                       I32, I32, I64, I32, I32, P]
     lib.pa_decode_cascade.restype = I32
@@ -296,3 +313,109 @@ def pa_swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor
                                            B, NS, ND, DTYPE_CODES[src_k.dtype],
                                            _stream_handle(stream, device))
     _check(rc, "pa_swap_blocks")
+
+
+class VirtualKV:
+    """KV storage on HIP virtual memory (pa_vkv_*): one contiguous virtual
+    range per request slot, physical pages mapped as sequences grow."""
+
+    def __init__(self, num_layers: int, max_batch: int, max_context_len: int, num_kv_heads: int,
+                 head_dim: int, dtype: torch.dtype, page_bytes: int = 0):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.pa_vkv_create(num_layers, max_batch, max_context_len, num_kv_heads, head_dim,
+                                 DTYPE_CODES[dtype], int(page_bytes), ctypes.byref(h)),
+               "pa_vkv_create")
+        self._h = h
+        self.num_layers, self.max_batch, self.max_context_len = num_layers, max_batch, \
+            max_context_len
+        self.num_kv_heads, self.head_dim, self.dtype = num_kv_heads, head_dim, dtype
+        info = self.info()
+        self.page_bytes = info["page_bytes"]
+        self.request_stride_blocks = info["request_stride_blocks"]
+
+    def _handle(self):
+        if self._h is None:
+            raise ValueError("VirtualKV is closed")
+        return self._h
+
+    def info(self) -> dict:
+        pb, rs, mb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        cu, mu = ctypes.c_double(), ctypes.c_double()
+        _check(load_library().pa_vkv_info(self._handle(), ctypes.byref(pb), ctypes.byref(rs),
+                                          ctypes.byref(mb), ctypes.byref(cu), ctypes.byref(mu)),
+               "pa_vkv_info")
+        return {"page_bytes": pb.value, "request_stride_blocks": rs.value,
+                "mapped_bytes": mb.value, "create_us_per_page": cu.value,
+                "map_us_per_page": mu.value}
+
+    def layer(self, layer: int):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(load_library().pa_vkv_layer(self._handle(), layer, ctypes.byref(k),
+                                           ctypes.byref(v)), "pa_vkv_layer")
+        return k.value, v.value
+
+    def alloc_reqid(self) -> int:
+        r = ctypes.c_int()
+        _check(load_library().pa_vkv_alloc_reqid(self._handle(), ctypes.byref(r)),
+               "pa_vkv_alloc_reqid")
+        return r.value
+
+    def step(self, seq_lens) -> None:
+        lens = (ctypes.c_int32 * self.max_batch)(*[int(x) for x in seq_lens])
+        _need(len(seq_lens) == self.max_batch, "seq_lens needs one entry per request slot")
+        _check(load_library().pa_vkv_step(self._handle(), lens), "pa_vkv_step")
+
+    def free_reqid(self, req_id: int) -> None:
+        _check(load_library().pa_vkv_free_reqid(self._handle(), req_id), "pa_vkv_free_reqid")
+
+    def reclaim(self) -> None:
+        _check(load_library().pa_vkv_reclaim(self._handle()), "pa_vkv_reclaim")
+
+    def close(self) -> None:
+        if self._h is not None:
+            _check(load_library().pa_vkv_destroy(self._h), "pa_vkv_destroy")
+            self._h = None
+
+    def slot(self, req_id: int, position: int) -> int:
+        """The slot of position `position` of request slot `req_id`."""
+        return req_id * self.request_stride_blocks * 16 + position
+
+    def write_kv(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                 slot_mapping: torch.Tensor, stream=None) -> None:
+        _need(k_new.shape == v_new.shape and k_new.dim() == 3
+              and tuple(k_new.shape[1:]) == (self.num_kv_heads, self.head_dim),
+              "k_new / v_new must be [T, Hkv, D]")
+        _need(k_new.dtype == v_new.dtype == self.dtype, "new tokens differ in dtype")
+        _need(k_new.is_cuda and k_new.is_contiguous() and v_new.is_contiguous(),
+              "new tokens must be contiguous on the GPU")
+        _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
+              and slot_mapping.shape[0] == k_new.shape[0] and slot_mapping.is_contiguous(),
+              "slot_mapping must be contiguous int64 [T]")
+        _check(load_library().pa_vkv_write_kv(self._handle(), layer, _ptr(k_new), _ptr(v_new),
+                                              _ptr(slot_mapping), k_new.shape[0],
+                                              _stream_handle(stream, k_new.device)),
+               "pa_vkv_write_kv")
+
+    def decode(self, layer: int, q: torch.Tensor, req_ids: torch.Tensor,
+               context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+               partition_tokens: int = 0, stream=None) -> None:
+        _need(q.dim() == 3 and q.shape[2] == self.head_dim and q.shape == out.shape,
+              "q and out must be [S, Hq, D]")
+        _need(q.dtype == out.dtype == self.dtype, "q and out differ in dtype")
+        _need(q.is_cuda and q.is_contiguous() and out.is_contiguous(), "q and out: contiguous GPU")
+        S = q.shape[0]
+        for t, name in ((req_ids, "req_ids"), (context_lens, "context_lens")):
+            _need(t.dtype == torch.int32 and tuple(t.shape) == (S,) and t.is_contiguous()
+                  and t.device == q.device, f"{name} must be contiguous int32 [S] on q's GPU")
+        _check(load_library().pa_vkv_decode(self._handle(), layer, _ptr(q), _ptr(req_ids),
+                                            _ptr(context_lens), float(scale), _ptr(out), S,
+                                            q.shape[1], int(partition_tokens),
+                                            _stream_handle(stream, q.device)),
+               "pa_vkv_decode")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -47,6 +47,18 @@ int elem_bytes(int dtype) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+}  // namespace
+
+namespace pa {
+int api_fail(int status, const char *msg) {
+    g_last_error = msg;
+    return status;
+}
+int api_hip_fail(hipError_t e, const char *where) { return hip_fail(e, where); }
+}  // namespace pa
+
+namespace {
+
 // ---- split workspace: one grow-only buffer per (device, stream) ------------
 // A buffer that a larger one replaces is kept, not freed, until
 // pa_release_workspaces: work already queued on the stream, and HIP graphs that
@@ -270,11 +282,17 @@ int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int
     return (int64_t)num_seqs * num_heads * np * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
-int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
-                 const int32_t *block_tables, const int32_t *context_lens, float scale,
-                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
-                 int partition_tokens, int flags, void *stream) {
+}  // extern "C"
+
+namespace pa {
+
+// pa_decode_ex, and the decode over virtual-memory storage (block_tables ==
+// nullptr, a Contiguous description instead).
+int decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, const int32_t *context_lens, float scale,
+                void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                int partition_tokens, int flags, void *stream, const Contiguous *contig) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -300,10 +318,12 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_blocks_per_seq too large");
     if (num_seqs == 0) return PA_OK;
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    if (!q || !k_cache || !v_cache || !(block_tables || contig) || !context_lens || !out ||
+        (contig && (!contig->req || !contig->mapped)))
         return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+        (contig && ((uintptr_t)contig->req & 3u)))
         return fail(PA_ERR_INVALID_ARG, "pa_decode: data pointers must be 16-byte aligned");
 
     const int G = num_heads / num_kv_heads;
@@ -349,6 +369,13 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
     a.NB = num_blocks;
     a.num_units = (int)units;
     a.shared_blocks = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
+    if (contig) {
+        a.bt = nullptr;
+        a.req = contig->req;
+        a.mapped = contig->mapped;
+        a.req_stride = contig->req_stride;
+        a.num_req = contig->num_req;
+    }
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
@@ -363,6 +390,21 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                                        (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(err, "pa_decode launch");
     return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                 int partition_tokens, int flags, void *stream) {
+    return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, num_blocks, dtype, partition_tokens, flags, stream,
+                           nullptr);
 }
 
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -30,7 +30,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
                                                        char *__restrict__ v_cache,
                                                        const int64_t *__restrict__ slots,
                                                        int64_t num_tokens, int Hkv, int D, int B,
-                                                       int64_t num_slots) {
+                                                       int64_t num_slots,
+                                                       const int *__restrict__ mapped,
+                                                       int req_stride, int num_req) {
     constexpr int X = 16 / E;
     // TT rows of D*E/4 words plus one pad word each: TT * D*E/4 <= 1024 and TT <= 256
     __shared__ uint32_t vtile[1024 + 256];
@@ -55,7 +57,13 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
         kv = ld16(k_new + src);
         vv = ld16(v_new + src);
     }
-    const bool ok = slot >= 0 && slot < num_slots;
+    bool ok = slot >= 0 && slot < num_slots;
+    if (ok && mapped) {  // virtual-memory storage: only positions with memory behind them
+        const int64_t per_req = (int64_t)req_stride * B;
+        const int64_t r = slot / per_req;
+        ok = r < num_req && slot - r * per_req < mapped[r];
+        if (!ok) slot = -1;
+    }
     if (ok) {
         const int64_t blk = slot / B;
         const int off = (int)(slot % B);
@@ -124,7 +132,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const char *__restrict
 
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
-                           int elem_bytes, hipStream_t stream) {
+                           int elem_bytes, hipStream_t stream, const int *mapped, int req_stride,
+                           int num_req) {
     if (T == 0) return hipSuccess;
     const int NC = D * elem_bytes / 16;  // <= 64 (head_dim <= 512 at 2 bytes, 256 at 4)
     const int TT = 256 / NC;
@@ -134,11 +143,11 @@ hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, 
     if (elem_bytes == 4) {
         write_kv_kernel<4><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
-            Hkv, D, B, NB * B);
+            Hkv, D, B, NB * B, mapped, req_stride, num_req);
     } else {
         write_kv_kernel<2><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
-            Hkv, D, B, NB * B);
+            Hkv, D, B, NB * B, mapped, req_stride, num_req);
     }
     return hipGetLastError();
 }

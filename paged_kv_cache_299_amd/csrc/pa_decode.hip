@@ -52,14 +52,34 @@ namespace pa {
 // Returns false past the last unit; otherwise s, its clamped context length
 // and the unit's rank r within its sequence (p = r / groups, g = r % groups).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool find_unit(int b, const int *ctx, int S, int cap, int P, int groups,
-                                          int &s_out, int &ctx_out, int &r_out) {
+// Context length of sequence s clamped to what its storage holds: the block
+// table's capacity, and with the contiguous layout the tokens mapped for its
+// request slot (a slot out of range holds none).
+__device__ __forceinline__ int seq_ctx(const DecodeArgs &a, int s) {
+    int cap = a.MB * kB;
+    if (!a.bt) {
+        const int r = a.req[s];
+        cap = (r >= 0 && r < a.num_req) ? min(cap, a.mapped[r]) : 0;
+    }
+    return clamp_ctx(a.ctx[s], cap);
+}
+
+// Physical block of logical block blk of sequence s (0 past the table).
+__device__ __forceinline__ int table_entry(const DecodeArgs &a, int s, int blk) {
+    if (blk >= a.MB) return 0;
+    if (a.bt) return a.bt[(int64_t)s * a.MB + blk];
+    return a.req[s] * a.req_stride + blk;  // only read when seq_ctx(s) > 0: r in range
+}
+
+__device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups, int &s_out,
+                                          int &ctx_out, int &r_out) {
+    const int S = a.S, P = a.P;
     const int lane = threadIdx.x & 63;
     int base = 0;
     for (int c0 = 0; c0 < S; c0 += 64) {
         const int s = c0 + lane;
         int u = 0;
-        const int c = s < S ? clamp_ctx(ctx[s], cap) : 0;
+        const int c = s < S ? seq_ctx(a, s) : 0;
         if (s < S) u = groups * (c > P ? (c + P - 1) / P : 1);
         // inclusive prefix sum over the wave
         int incl = u;
@@ -125,16 +145,14 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
-    const int cap = a.MB * kB;
-
     int s, ctx, r;
-    if (!find_unit(blockIdx.x, a.ctx, a.S, cap, a.P, a.Hkv, s, ctx, r)) return;
+    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
     const int per = blocks_per_partition(ctx, a.P);
     const int blk0 = p * per;
     const int t0 = blk0 * kB;
-    int my_bt = blk0 + lane < a.MB ? a.bt[(int64_t)s * a.MB + blk0 + lane] : 0;
+    int my_bt = table_entry(a, s, blk0 + lane);
 
     // column n -> query head of the group; in SPLIT mode columns G..2G-1
     // repeat heads 0..G-1 (they take the lo parts of the weights)
@@ -371,7 +389,7 @@ void decode_valu_kernel(const DecodeArgs a) {
     // Units in the order of find_unit (sequence-major, head fastest).  With a
     // multiple of 8 heads, head h of a sequence runs on XCD (offset + h) % 8.
     int s, ctx, r;
-    if (!find_unit(blockIdx.x, a.ctx, a.S, a.MB * kB, a.P, a.Hq, s, ctx, r)) return;
+    if (!find_unit(blockIdx.x, a, a.Hq, s, ctx, r)) return;
     const int h = r % a.Hq;
     const int p = r / a.Hq;
     const int g = h / a.G;
@@ -379,7 +397,7 @@ void decode_valu_kernel(const DecodeArgs a) {
     const int per = blocks_per_partition(ctx, a.P);
     const int blk0 = p * per;
     const int t0 = blk0 * kB;
-    int my_bt = blk0 + lane < a.MB ? a.bt[(int64_t)s * a.MB + blk0 + lane] : 0;
+    int my_bt = table_entry(a, s, blk0 + lane);
     char *outp = (char *)a.out + ((int64_t)s * a.Hq + h) * D * E;
     if (t0 >= ctx) {
         if (p == 0) {
@@ -521,7 +539,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a
             ov[q] = *(const f32x4 *)(po + (int64_t)q * D);
         }
     }
-    const int ctx = clamp_ctx(a.ctx[s], a.MB * kB);
+    const int ctx = seq_ctx(a, s);
     const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
     if (np <= 1) return;  // written by the partition kernel
     float M = -INFINITY, L = 0.f;

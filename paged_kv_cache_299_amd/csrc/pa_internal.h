@@ -23,6 +23,13 @@ struct DecodeArgs {
     int64_t NB;
     int num_units;          // workgroups of the launch: an upper bound on the units
     int shared_blocks;      // MFMA kernel: K/V with cacheable loads (blocks read by several sequences)
+    // Contiguous layout (bt == nullptr): sequence s uses request slot req[s],
+    // whose blocks are req[s] * req_stride + 0, 1, ...; mapped[r] tokens of
+    // slot r are backed by memory (virtual-memory KV storage).
+    const int *req;         // [S]
+    const int *mapped;      // [num_req]
+    int req_stride;
+    int num_req;
 };
 
 enum class DecodeKernel { kValu, kMfma };
@@ -75,12 +82,33 @@ struct CascadeArgs {
 hipError_t launch_cascade(const CascadeArgs &a, int dtype, int head_dim, int grid,
                           hipStream_t stream);
 
+// mapped != nullptr: a slot is stored only if its request slot
+// (slot / (req_stride * B)) has memory behind its position (< mapped[r] tokens).
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
-                           int elem_bytes, hipStream_t stream);
+                           int elem_bytes, hipStream_t stream, const int *mapped = nullptr,
+                           int req_stride = 0, int num_req = 0);
 
 hipError_t launch_copy_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
                               const int64_t *pairs, int64_t n, int64_t src_blocks,
                               int64_t dst_blocks, int64_t block_bytes, hipStream_t stream);
+
+// Contiguous (virtual-memory) KV layout for decode_impl.
+struct Contiguous {
+    const int *req;     // [S] request slot of each sequence (device)
+    const int *mapped;  // [num_req] tokens with memory behind them (device)
+    int req_stride;     // blocks between consecutive request slots
+    int num_req;
+};
+
+int decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, const int32_t *context_lens, float scale,
+                void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                int partition_tokens, int flags, void *stream, const Contiguous *contig);
+
+// Record the message pa_last_error() returns on this thread; returns status.
+int api_fail(int status, const char *msg);
+int api_hip_fail(hipError_t e, const char *where);
 
 }  // namespace pa

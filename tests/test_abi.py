@@ -187,6 +187,32 @@ def test_cascade_argument_checks(kw, status):
         assert "pa_decode_cascade" in lib.pa_last_error().decode()
 
 
+def test_vkv_argument_checks():
+    """The virtual-memory KV calls check their host arguments before any HIP
+    call, and every call rejects a null handle."""
+    lib = pa.load_library()
+    h = ctypes.c_void_p(123)
+    for args in [(0, 4, 1024, 8, 128, BF16, 0), (2, 0, 1024, 8, 128, BF16, 0),
+                 (2, 4, 1000, 8, 128, BF16, 0), (2, 4, 1024, 8, 128, 9, 0),
+                 (2, 4, 1024, 8, 12, BF16, 0), (2, 4, 1024, 8, 128, BF16, -1)]:
+        assert lib.pa_vkv_create(*args, ctypes.byref(h)) == INVALID, args
+        assert h.value is None
+    assert lib.pa_vkv_create(2, 4, 1024, 8, 128, BF16, 0, None) == INVALID
+    null = None
+    r = ctypes.c_int()
+    assert lib.pa_vkv_alloc_reqid(null, ctypes.byref(r)) == INVALID
+    assert lib.pa_vkv_free_reqid(null, 0) == INVALID
+    assert lib.pa_vkv_step(null, None) == INVALID
+    assert lib.pa_vkv_reclaim(null) == INVALID
+    assert lib.pa_vkv_info(null, None, None, None, None, None) == INVALID
+    assert lib.pa_vkv_destroy(null) == OK
+    assert lib.pa_vkv_write_kv(null, 0, A_, A_, A_, 1, None) == INVALID
+    assert lib.pa_vkv_decode(null, 0, A_, A_, A_, 0.1, A_, 1, 8, 0, None) == INVALID
+
+
+A_ = ALIGNED
+
+
 def test_workspace_size_query():
     lib = pa.load_library()
     # 32 seqs x 32 heads x ceil(4096/256) partitions x (128 + 2) floats
