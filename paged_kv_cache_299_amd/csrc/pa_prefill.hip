@@ -28,9 +28,11 @@
 //    A operand is two 8-byte reads of the transposed V tiles at the same
 //    keys.  The weights go in as hi + lo 16-bit parts (hi = RNE(p),
 //    lo = RNE(p - hi)), so P keeps about 16 significant bits.
-// K/V are loaded one iteration ahead with plain (cacheable) loads: the other
-// waves of the workgroup and the other row tiles of the sequence read the
-// same tiles.
+// K/V go through one set of operand registers (228 VGPRs, two waves per
+// SIMD): the next K is requested as soon as the scores are in, the next V as
+// soon as the P.V products have read the current one.  Plain (cacheable)
+// loads: the other waves of the workgroup and the other row tiles of the
+// sequence read the same tiles.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -45,7 +47,8 @@ constexpr int kRowsPerGroup = kPrefillWaves * kRowsPerWave;  // 128
 constexpr int kBtChunk = 64;                                 // table entries per lane load
 
 template <int DT, int D>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(const PrefillArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
     constexpr int NKC = D / 32;       // QK steps of 32 dims
@@ -116,14 +119,22 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         for (int t = 0; t < NVT; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    struct Ops {
-        i32x4 k[2][NKC];
-        i32x2 v[2][NVT];
-    };
-    Ops b0, b1;
+    // One set of operand registers: the K of the next two blocks is requested
+    // as soon as the scores of the current ones are in, their V as soon as
+    // the current P.V products have read theirs.  (A second set, to request a
+    // whole iteration ahead, took the kernel to 352 registers and one wave
+    // per SIMD.)
+    i32x4 kk[2][NKC];
+    i32x2 vv[2][NVT];
     // Iteration it reads blocks 2 it and 2 it + 1; a block past the wave's
     // last one gets a zero-range descriptor (zeros, no memory traffic).
-    auto load = [&](Ops &x, int it) {
+    auto tile_off = [&](int it, int b, bool &in) {
+        const int blk = 2 * it + b;
+        in = blk < nblk;
+        const int phys = __builtin_amdgcn_readlane(my_bt, in ? (blk & (kBtChunk - 1)) : 0);
+        return (int64_t)phys * blk_stride;
+    };
+    auto load_k = [&](int it) {
         if ((it & (kBtChunk / 2 - 1)) == 0) {  // next slice of the block table
             const int e = 2 * it + lane;
             int id = e < nblk ? btrow[e] : 0;
@@ -132,23 +143,29 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
         }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int blk = 2 * it + b;
-            const bool in = blk < nblk;
-            const int phys = __builtin_amdgcn_readlane(my_bt, in ? (blk & (kBtChunk - 1)) : 0);
-            const int64_t off = (int64_t)phys * blk_stride;
+            bool in;
+            const int64_t off = tile_off(it, b, in);
             const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
-            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
             for (int c = 0; c < NKC; ++c)
-                x.k[b][c] = bload16<kCachePolicyPlain>(rk, (64 * c + lane) * 16);
+                kk[b][c] = bload16<kCachePolicyPlain>(rk, (64 * c + lane) * 16);
+        }
+        issue_point();
+    };
+    auto load_v = [&](int it) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            bool in;
+            const int64_t off = tile_off(it, b, in);
+            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
             for (int t = 0; t < NVT; ++t)
-                x.v[b][t] = bload8<kCachePolicyPlain>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+                vv[b][t] = bload8<kCachePolicyPlain>(rv, ((16 * t + n) * kB + 4 * j) * 2);
         }
         issue_point();
     };
 
-    auto step = [&](Ops &x, Ops &y, int it) {
+    auto step = [&](int it) {
         f32x4 sc[kRowTiles][2];
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt)
@@ -156,9 +173,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
             for (int b = 0; b < 2; ++b) {
                 sc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < NKC; ++c) sc[rt][b] = mfma32<DT>(x.k[b][c], qf[rt][c], sc[rt][b]);
+                for (int c = 0; c < NKC; ++c) sc[rt][b] = mfma32<DT>(kk[b][c], qf[rt][c], sc[rt][b]);
             }
-        load(y, it + 1);
+        load_k(it + 1);
         const int key0 = 32 * it;
         // slots at or past ctx (the tail of the sequence's last block) may hold
         // NaN: their V is zeroed, since a zero weight does not cancel a NaN
@@ -170,15 +187,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
                 const uint32_t m1 = (kb + 2 < ctx ? 0x0000ffffu : 0u) | (kb + 3 < ctx ? 0xffff0000u : 0u);
 #pragma unroll
                 for (int t = 0; t < NVT; ++t)
-                    x.v[b][t] = i32x2{(int)((uint32_t)x.v[b][t][0] & m0),
-                                      (int)((uint32_t)x.v[b][t][1] & m1)};
+                    vv[b][t] = i32x2{(int)((uint32_t)vv[b][t][0] & m0),
+                                     (int)((uint32_t)vv[b][t][1] & m1)};
             }
         }
-        i32x4 va[NVT];
-#pragma unroll
-        for (int t = 0; t < NVT; ++t)
-            va[t] = i32x4{x.v[0][t][0], x.v[0][t][1], x.v[1][t][0], x.v[1][t][1]};
         const bool full = key0 + 31 <= p_min;  // no key of the iteration is masked for any row
+        uint32_t hi[kRowTiles][4], lo[kRowTiles][4];
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt) {
             float sv[8];
@@ -217,30 +231,30 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
                         if (key0 + 16 * b + 4 * j + e > prow[rt]) pe[4 * b + e] = 0.f;
             }
             l[rt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-            uint32_t hi[4], lo[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                hi[w] = pack2<DT>(pe[2 * w], pe[2 * w + 1]);
-                lo[w] = pack2<DT>(pe[2 * w] - elem_lo<DT>(hi[w]), pe[2 * w + 1] - elem_hi<DT>(hi[w]));
-            }
-            const i32x4 phi = {(int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            const i32x4 plo = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3]};
-#pragma unroll
-            for (int t = 0; t < NVT; ++t) {
-                o[rt][t] = mfma32<DT>(va[t], phi, o[rt][t]);
-                o[rt][t] = mfma32<DT>(va[t], plo, o[rt][t]);
+                hi[rt][w] = pack2<DT>(pe[2 * w], pe[2 * w + 1]);
+                lo[rt][w] = pack2<DT>(pe[2 * w] - elem_lo<DT>(hi[rt][w]),
+                                      pe[2 * w + 1] - elem_hi<DT>(hi[rt][w]));
             }
         }
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const i32x4 va = {vv[0][t][0], vv[0][t][1], vv[1][t][0], vv[1][t][1]};
+#pragma unroll
+            for (int rt = 0; rt < kRowTiles; ++rt) {
+                const i32x4 phi = {(int)hi[rt][0], (int)hi[rt][1], (int)hi[rt][2], (int)hi[rt][3]};
+                const i32x4 plo = {(int)lo[rt][0], (int)lo[rt][1], (int)lo[rt][2], (int)lo[rt][3]};
+                o[rt][t] = mfma32<DT>(va, phi, o[rt][t]);
+                o[rt][t] = mfma32<DT>(va, plo, o[rt][t]);
+            }
+        }
+        load_v(it + 1);
     };
 
-    // one exit, at the loop test (see the decode kernel)
-    load(b0, 0);
-    int it = 0;
-    for (; it + 2 <= iters; it += 2) {
-        step(b0, b1, it);
-        step(b1, b0, it + 1);
-    }
-    if (it < iters) step(b0, b1, it);
+    load_k(0);
+    load_v(0);
+    for (int it = 0; it < iters; ++it) step(it);
 
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
