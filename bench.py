@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--cascade", action="store_true",
                     help="decode with pa_decode_cascade: shared prefix blocks read once per "
                          "group of sequences (groups from the block tables)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per block for the llama3_8b workload (8, 16 or 32)")
     ap.add_argument("--page-kib", type=int, default=2048,
                     help="page size of the virtual-memory KV storage (vattention workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -186,8 +188,10 @@ def main():
         return
 
     t_setup = time.time()
-    case = workloads.CASES[args.workload](
-        fill=False, **({} if args.seed is None else {"seed": args.seed}))
+    kw = {} if args.seed is None else {"seed": args.seed}
+    if args.block_size is not None:
+        kw["block_size"] = args.block_size
+    case = workloads.CASES[args.workload](fill=False, **kw)
     S, Hq, Hkv, D, B = case.num_seqs, case.num_heads, case.num_kv_heads, case.head_dim, \
         case.block_size
     NB, dt = case.num_blocks, case.dtype
@@ -300,7 +304,8 @@ def main():
     # roofline bytes: each physical block counted once (equal to dec_bytes
     # unless blocks are shared; then the logical rate is reported as effective)
     achieved = uniq_bytes / (dec_avg * 1e-3) / 1e9
-    traffic, traffic_src = (None, None) if args.cascade else measured_traffic(args.workload, part)
+    traffic, traffic_src = ((None, None) if args.cascade or B != 16
+                            else measured_traffic(args.workload, part))
 
     # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
     cpu = None
@@ -341,7 +346,8 @@ def main():
         "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[dt],
         "data": "synthetic (seeded N(0,1) K/V/q, seeded block placement and context lengths)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + (
+                       f" (blocks of {B} tokens)" if B != 16 else ""), "name": args.workload,
                    "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
                    "seed": case.seed, "partition_tokens": part or "auto",

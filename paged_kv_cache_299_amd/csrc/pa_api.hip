@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -309,9 +310,19 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG,
                     "pa_decode: partition_tokens %d must be 0 or a multiple of 16 in [16, %d]",
                     partition_tokens, kMaxPartition);
-    if (block_size != kBlock)
-        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (only 16 is built)",
+    const bool mfma_ok = dtype != PA_F32 && num_heads / num_kv_heads <= 16;
+    if (block_size != kBlock && !((block_size == 8 || block_size == 32) && mfma_ok && !contig))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (16 is built for every case; "
+                    "8 and 32 for 16-bit data with at most 16 query heads per kv head)",
                     block_size);
+    // block size 8: a unit's table slice is 64 entries = 512 tokens, and the
+    // kernel addresses the pool with 32-bit offsets
+    const int max_part = block_size == 8 ? 512 : kMaxPartition;
+    if (block_size == 8 && partition_tokens > max_part)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size 8 takes partition_tokens <= 512");
+    if (block_size == 8 &&
+        num_blocks * (int64_t)num_kv_heads * head_dim * block_size * e > 0x7fff0000LL)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size 8 takes pools under 2 GiB");
     if (head_dim != 64 && head_dim != 128)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (64 and 128 are built)",
                     head_dim);
@@ -327,20 +338,22 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "pa_decode: data pointers must be 16-byte aligned");
 
     const int G = num_heads / num_kv_heads;
-    const int max_tokens = max_blocks_per_seq * kBlock;
+    const int max_tokens = max_blocks_per_seq * block_size;
     const bool mfma = dtype != PA_F32 && G <= 16;
 
     int P = partition_tokens > 0
                 ? partition_tokens
-                : auto_partition(mfma, (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
-                                 max_tokens);
+                : std::min(auto_partition(mfma,
+                                          (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
+                                          max_tokens),
+                           max_part);
     int64_t NP = 1;
     if (P < max_tokens) {
         NP = num_partitions(max_tokens, P);
     } else {
         // one partition covers every sequence; keep P a multiple of 16 that does
         P = max_tokens < kBlock ? kBlock : (max_tokens + kBlock - 1) / kBlock * kBlock;
-        if (P > kMaxPartition) P = kMaxPartition, NP = num_partitions(max_tokens, P);
+        if (P > max_part) P = max_part, NP = num_partitions(max_tokens, P);
     }
     if (NP > kMaxPartitions)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld partitions (max %d)", (long long)NP,
@@ -367,6 +380,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
     a.NP = (int)NP;
     a.P = P;
     a.NB = num_blocks;
+    a.BS = block_size;
     a.num_units = (int)units;
     a.shared_blocks = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
     if (contig) {

@@ -56,7 +56,7 @@ namespace pa {
 // table's capacity, and with the contiguous layout the tokens mapped for its
 // request slot (a slot out of range holds none).
 __device__ __forceinline__ int seq_ctx(const DecodeArgs &a, int s) {
-    int cap = a.MB * kB;
+    int cap = a.MB * a.BS;
     if (!a.bt) {
         const int r = a.req[s];
         cap = (r >= 0 && r < a.num_req) ? min(cap, a.mapped[r]) : 0;
@@ -133,14 +133,22 @@ __device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups
 // per tile whose range is empty past the unit's last block, so the request
 // needs no branch and the one past the end makes no memory traffic.
 // ---------------------------------------------------------------------------
-template <int DT, int D, bool SPLIT, int POLICY>
+//
+// Block sizes 8 and 32 (BS): the kernel still works in steps of 16 tokens.
+// With BS = 32 a step is one half of a block (the tile of the block's kv head
+// is [D/8][32][8] and [D][32]); with BS = 8 a step spans two blocks, and each
+// lane addresses the block of its own tokens through a whole-pool descriptor
+// (32-bit offsets: pools under 4 GiB), a step past the end getting offsets
+// outside the descriptor's range.
+template <int DT, int D, bool SPLIT, int POLICY, int BS = 16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
     constexpr int NKC = D / 32;       // QK steps, 32 dims each
     constexpr int NVT = D / 16;       // P.V output tiles, 16 dims each
-    constexpr int TILE = D * kB * 2;  // bytes of one (block, kv head) tile
+    constexpr int TILE = D * BS * 2;  // bytes of one (block, kv head) tile
 
     const int lane = threadIdx.x;
     const int n = lane & 15;
@@ -150,9 +158,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
     const int per = blocks_per_partition(ctx, a.P);
-    const int blk0 = p * per;
+    const int blk0 = p * per;  // in steps of 16 tokens
     const int t0 = blk0 * kB;
-    int my_bt = table_entry(a, s, blk0 + lane);
+    const int e0 = t0 / BS;    // the unit's first table entry
+    int my_bt = table_entry(a, s, e0 + lane);
 
     // column n -> query head of the group; in SPLIT mode columns G..2G-1
     // repeat heads 0..G-1 (they take the lo parts of the weights)
@@ -169,10 +178,11 @@ void decode_mfma_kernel(const DecodeArgs a) {
         return;
     }
     const int t1 = min(ctx, t0 + per * kB);
-    const int nblk = (t1 - t0 + kB - 1) / kB;  // 1..64
+    const int nblk = (t1 - t0 + kB - 1) / kB;  // 16-token steps, 1..64 (1..32 at BS = 8)
+    const int nent = (t1 + BS - 1) / BS - e0;  // table entries of the unit
     // entries past the context are never used; out-of-range ids are clamped so
     // that no read leaves the pool
-    if (lane >= nblk || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
+    if (lane >= nent || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
 
     const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)s * a.Hq + h) * D;
     i32x4 qf[NKC];
@@ -196,16 +206,54 @@ void decode_mfma_kernel(const DecodeArgs a) {
         i32x2 v[NVT];
     };
     Blk b0, b1;
+    // (BS = 8: descriptors over the rest of the pool from this kv head's first tile)
+    const int pool_left = BS == 8 ? (int)min<int64_t>(a.NB * blk_stride - (int64_t)g * TILE,
+                                                        0x7fffffff)
+                                  : 0;
+    const auto rk8 = tile_rsrc(kbase, pool_left);
+    const auto rv8 = tile_rsrc(vbase, pool_left);
     auto load = [&](Blk &x, int i) {
         const bool in = i < nblk;
-        const int phys = __builtin_amdgcn_readlane(my_bt, in ? i : 0);
-        const int64_t off = (int64_t)phys * blk_stride;
-        const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
-        const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
+        if constexpr (BS == 16) {
+            const int phys = __builtin_amdgcn_readlane(my_bt, in ? i : 0);
+            const int64_t off = (int64_t)phys * blk_stride;
+            const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) x.k[c] = bload16<POLICY>(rk, (64 * c + lane) * 16);
+            for (int c = 0; c < NKC; ++c) x.k[c] = bload16<POLICY>(rk, (64 * c + lane) * 16);
 #pragma unroll
-        for (int t = 0; t < NVT; ++t) x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+            for (int t = 0; t < NVT; ++t)
+                x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+        } else if constexpr (BS == 32) {
+            const int tok = t0 + kB * i;           // first token of the step
+            const int e = in ? tok / BS - e0 : 0;  // its block, and which half
+            const int half = (tok / kB) & 1;
+            const int phys = __builtin_amdgcn_readlane(my_bt, e);
+            const int64_t off = (int64_t)phys * blk_stride;
+            const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
+#pragma unroll
+            for (int c = 0; c < NKC; ++c)
+                x.k[c] = bload16<POLICY>(rk, ((4 * c + j) * BS + kB * half + n) * 16);
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+                x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * BS + kB * half + 4 * j) * 2);
+        } else {
+            const int tok = t0 + kB * i;
+            const int e = in ? tok / BS - e0 : 0;  // the step's two blocks: e, e + 1
+            const int p0 = __builtin_amdgcn_readlane(my_bt, e);
+            const int p1 = __builtin_amdgcn_readlane(my_bt, in ? e + 1 : 0);
+            // tokens n < 8 (K) and 4j < 8 (V) are in the first block
+            const int kofs = (n < 8 ? p0 : p1) * (int)blk_stride;
+            const int vofs = (j < 2 ? p0 : p1) * (int)blk_stride;
+            const int none = 0x7fffffff;  // outside the descriptor: zeros, no traffic
+#pragma unroll
+            for (int c = 0; c < NKC; ++c)
+                x.k[c] = bload16<POLICY>(rk8, in ? kofs + ((4 * c + j) * BS + (n & 7)) * 16 : none);
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+                x.v[t] = bload8<POLICY>(rv8, in ? vofs + ((16 * t + n) * BS + 4 * (j & 1)) * 2 : none);
+        }
         issue_point();
     };
 
@@ -568,7 +616,20 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
     const int grid = a.num_units;
     if (grid > 0) {
         if constexpr (DT != kF32) {
-            if (kind == DecodeKernel::kMfma) {
+            if (kind == DecodeKernel::kMfma && a.BS != kB) {
+                const bool split = 2 * a.G <= 16;
+                if (a.BS == 32) {
+                    if (split)
+                        decode_mfma_kernel<DT, D, true, kCachePolicyNT, 32><<<grid, 64, 0, stream>>>(a);
+                    else
+                        decode_mfma_kernel<DT, D, false, kCachePolicyNT, 32><<<grid, 64, 0, stream>>>(a);
+                } else {
+                    if (split)
+                        decode_mfma_kernel<DT, D, true, kCachePolicyNT, 8><<<grid, 64, 0, stream>>>(a);
+                    else
+                        decode_mfma_kernel<DT, D, false, kCachePolicyNT, 8><<<grid, 64, 0, stream>>>(a);
+                }
+            } else if (kind == DecodeKernel::kMfma) {
                 const bool split = 2 * a.G <= 16;
                 if (a.shared_blocks) {
                     if (split)

@@ -20,6 +20,7 @@ struct DecodeArgs {
     float scale_log2_abs;   // |scale| * log2(e)
     int q_xor;              // 0x80008000 when scale < 0: flips the sign of 16-bit q
     int S, Hq, Hkv, G, MB, NP, P;
+    int BS;                 // tokens per block: 16, or 8 / 32 (matrix-core kernel only)
     int64_t NB;
     int num_units;          // workgroups of the launch: an upper bound on the units
     int shared_blocks;      // MFMA kernel: K/V with cacheable loads (blocks read by several sequences)

@@ -165,12 +165,15 @@ def tiny(seed: int = 1, fill: bool = True) -> DecodeCase:
                             dtype=torch.float32, fill=fill)
 
 
-def llama3_8b(seed: int = 2, num_seqs: int = 32, fill: bool = True) -> DecodeCase:
+def llama3_8b(seed: int = 2, num_seqs: int = 32, fill: bool = True,
+              block_size: int = 16) -> DecodeCase:
+    """Block sizes other than 16 keep the pool's token capacity (12,000 x 16)."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(128, 4096, size=num_seqs, endpoint=True)
     return make_decode_case("llama3_8b", seed=seed, context_lens=ctx, num_heads=32,
-                            num_kv_heads=8, head_dim=128, block_size=16, num_blocks=12000,
-                            max_blocks=256, dtype=torch.bfloat16, rng=rng, fill=fill)
+                            num_kv_heads=8, head_dim=128, block_size=block_size,
+                            num_blocks=12000 * 16 // block_size, max_blocks=4096 // block_size,
+                            dtype=torch.bfloat16, rng=rng, fill=fill)
 
 
 def opt_13b(seed: int = 3, num_seqs: int = 64, fill: bool = True) -> DecodeCase:

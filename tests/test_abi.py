@@ -59,7 +59,11 @@ def _decode(lib, **kw):
     (dict(P=20), INVALID),
     (dict(P=2048), INVALID),
     (dict(flags=2), INVALID),
-    (dict(B=32), UNSUPPORTED),
+    (dict(B=24), UNSUPPORTED),
+    (dict(B=32, dtype=F32), UNSUPPORTED),        # block sizes 8 / 32: matrix-core kernel only
+    (dict(B=32, Hq=136, Hkv=4), UNSUPPORTED),    # more than 16 query heads per kv head
+    (dict(B=8, P=1024), UNSUPPORTED),            # block size 8: partitions up to 512 tokens
+    (dict(B=8, NB=300000), UNSUPPORTED),         # block size 8: pools under 2 GiB
     (dict(D=96), UNSUPPORTED),
     (dict(q=None), INVALID),
     (dict(out=ctypes.c_void_p((1 << 20) + 2)), INVALID),

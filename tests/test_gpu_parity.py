@@ -275,3 +275,48 @@ def test_graph_replay_matches_eager(dev):
         with torch.cuda.stream(stream):
             finer = g.decode(16 if rep == 0 else 32)
         check_decode(finer, ref, case.dtype, f"finer split after replay {rep}", strict=False)
+
+
+# --------------------------------------------------------------------------
+# block sizes 8 and 32 (matrix-core kernel): a step of 16 tokens spans two
+# blocks, or half of one
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (16, 1), (8, 4)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_sizes_8_and_32(dev, B, dtype, Hq, Hkv, D):
+    ctxs = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 513, 1000, 0]
+    need = sum(-(-c // B) for c in ctxs)
+    case = workloads.make_decode_case("edge", seed=B * 100 + Hq + D, context_lens=ctxs,
+                                      num_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                                      num_blocks=need + 9, max_blocks=-(-1000 // B),
+                                      dtype=dtype)
+    log(f"block size {B} {dtype} Hq={Hq} Hkv={Hkv} D={D}")
+    g, ref, _ = run_full_case(case, dev, 0, strict=False)
+    for P in (16, 48, 512):
+        out = g.decode(P)
+        check_decode(out, ref, dtype, f"B={B} P={P}")
+
+
+@pytest.mark.parametrize("B", [8, 32])
+def test_block_sizes_full_size_llama(dev, B):
+    """The Llama-3-8B-shaped batch stored in blocks of 8 or 32 tokens."""
+    case = workloads.llama3_8b(block_size=B)
+    run_full_case(case, dev, 0, strict=True)
+
+
+def test_block_size_limits_are_reported(dev):
+    """Block sizes the kernels do not take give PA_ERR_UNSUPPORTED, not a launch."""
+    case = workloads.make_decode_case("edge", seed=5, context_lens=[40], num_heads=4,
+                                      num_kv_heads=1, head_dim=64, block_size=8, num_blocks=8,
+                                      max_blocks=5, dtype=torch.bfloat16)
+    g = GpuCase(case, dev)
+    with pytest.raises(pa.PAError):
+        g.decode(1024)      # block size 8 takes partitions up to 512 tokens
+    case32 = workloads.make_decode_case("edge", seed=5, context_lens=[40], num_heads=32,
+                                        num_kv_heads=1, head_dim=64, block_size=32, num_blocks=4,
+                                        max_blocks=2, dtype=torch.bfloat16)
+    g32 = GpuCase(case32, dev)
+    with pytest.raises(pa.PAError):
+        g32.decode()        # 32 query heads per kv head run on the VALU kernel: B = 16 only
