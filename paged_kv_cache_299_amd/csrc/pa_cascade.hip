@@ -172,10 +172,10 @@ __device__ __forceinline__ void cascade_unit(const CascadeArgs &a, int r, int ra
         const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
         const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) x.k[c] = bload16<kCachePolicyPlain>(rk, (64 * c + lane) * 16);
+        for (int c = 0; c < NKC; ++c) x.k[c] = bload16<kCachePolicyNT>(rk, (64 * c + lane) * 16);
 #pragma unroll
         for (int t = 0; t < NVT; ++t)
-            x.v[t] = bload8<kCachePolicyPlain>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+            x.v[t] = bload8<kCachePolicyNT>(rv, ((16 * t + n) * kB + 4 * j) * 2);
         issue_point();
     };
 
@@ -252,7 +252,11 @@ __device__ __forceinline__ void cascade_unit(const CascadeArgs &a, int r, int ra
 template <int DT, int D>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void cascade_kernel(const CascadeArgs a) {
-    for (int b = blockIdx.x;; b += gridDim.x) {
+    // Rounds of gridDim.x units, in alternating directions: the list holds
+    // the (longer) prefix units first, so a wave that took a prefix unit in
+    // one round takes one of the last units of the next.
+    for (int round = 0;; ++round) {
+        const int b = round * gridDim.x + ((round & 1) ? gridDim.x - 1 - blockIdx.x : blockIdx.x);
         int r, rank;
         if (!find_cascade_unit(a, b, r, rank)) return;
         cascade_unit<DT, D>(a, r, rank);
