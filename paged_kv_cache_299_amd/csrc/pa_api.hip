@@ -320,6 +320,9 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
     const int max_part = block_size == 8 ? 512 : kMaxPartition;
     if (block_size == 8 && partition_tokens > max_part)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size 8 takes partition_tokens <= 512");
+    if (block_size == 32 && partition_tokens % 32 != 0)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size 32 takes partition_tokens that "
+                    "are multiples of 32");
     if (block_size == 8 &&
         num_blocks * (int64_t)num_kv_heads * head_dim * block_size * e > 0x7fff0000LL)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size 8 takes pools under 2 GiB");

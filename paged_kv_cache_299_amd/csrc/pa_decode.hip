@@ -134,18 +134,17 @@ __device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups
 // needs no branch and the one past the end makes no memory traffic.
 // ---------------------------------------------------------------------------
 //
-// Block sizes 8 and 32 (BS): the kernel still works in steps of 16 tokens.
-// With BS = 32 a step is one half of a block (the tile of the block's kv head
-// is [D/8][32][8] and [D][32]); with BS = 8 a step spans two blocks, and each
-// lane addresses the block of its own tokens through a whole-pool descriptor
-// (32-bit offsets: pools under 4 GiB), a step past the end getting offsets
-// outside the descriptor's range.
+// Block size 8 (BS): the kernel still works in steps of 16 tokens; a step
+// spans two blocks, and each lane addresses the block of its own tokens
+// through a whole-pool descriptor (32-bit offsets: pools under 2 GiB), a step
+// past the end getting offsets outside the descriptor's range.  (Block size
+// 32 has a kernel of its own below, with whole-block steps.)
 template <int DT, int D, bool SPLIT, int POLICY, int BS = 16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
-    static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+    static_assert(BS == 8 || BS == 16, "block size");
     constexpr int NKC = D / 32;       // QK steps, 32 dims each
     constexpr int NVT = D / 16;       // P.V output tiles, 16 dims each
     constexpr int TILE = D * BS * 2;  // bytes of one (block, kv head) tile
@@ -224,20 +223,6 @@ void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < NVT; ++t)
                 x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * kB + 4 * j) * 2);
-        } else if constexpr (BS == 32) {
-            const int tok = t0 + kB * i;           // first token of the step
-            const int e = in ? tok / BS - e0 : 0;  // its block, and which half
-            const int half = (tok / kB) & 1;
-            const int phys = __builtin_amdgcn_readlane(my_bt, e);
-            const int64_t off = (int64_t)phys * blk_stride;
-            const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
-            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
-#pragma unroll
-            for (int c = 0; c < NKC; ++c)
-                x.k[c] = bload16<POLICY>(rk, ((4 * c + j) * BS + kB * half + n) * 16);
-#pragma unroll
-            for (int t = 0; t < NVT; ++t)
-                x.v[t] = bload8<POLICY>(rv, ((16 * t + n) * BS + kB * half + 4 * j) * 2);
         } else {
             const int tok = t0 + kB * i;
             const int e = in ? tok / BS - e0 : 0;  // the step's two blocks: e, e + 1
@@ -342,6 +327,205 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const float lt = xor32_sum(xor16_sum(l));  // all lanes take part in the swaps
     if (!hi_col) return;
     if (t0 == 0 && t1 == ctx) {  // the unit covers the whole context
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) store4<DT>(outp + 16 * t + 4 * j, o[t], inv);
+        return;
+    }
+    const int64_t part = ((int64_t)s * a.Hq + h) * a.NP + p;
+    float *po = a.part_o + part * D;
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
+    if (j == 0) *(float2 *)(a.part_ml + 2 * part) = float2{m, lt};
+}
+
+// ---------------------------------------------------------------------------
+// Block size 32 on MFMA: a step is one whole block.  The scores of its two
+// 16-token halves come from two products per 32 dims; the P.V product is one
+// 16x16x32 per output tile whose k slots 8j .. 8j+7 hold keys 4j .. 4j+3 of
+// the first half and of the second, which is what lane group j holds of P^T
+// and what its two 8-byte V reads at the same keys give (both halves of each
+// V row in one step).  Partitions are whole blocks: P is a multiple of 32.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool SPLIT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_mfma_b32_kernel(const DecodeArgs a) {
+    static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
+    constexpr int BS = 32;
+    constexpr int NKC = D / 32;
+    constexpr int NVT = D / 16;
+    constexpr int TILE = D * BS * 2;
+
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    int s, ctx, r;
+    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
+    const int g = r % a.Hkv;
+    const int p = r / a.Hkv;
+    // ceil(ctx / P) partitions of equal whole blocks (ceil(nb / per) of them are
+    // non-empty, which is that count since P is a multiple of the block)
+    const int nb = (ctx + BS - 1) / BS;
+    const int npart = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
+    const int per = (nb + npart - 1) / npart;
+    const int blk0 = p * per;
+    const int t0 = blk0 * BS;
+    int my_bt = table_entry(a, s, blk0 + lane);
+
+    const bool hi_col = n < a.G;
+    const bool col_ok = SPLIT ? n < 2 * a.G : hi_col;
+    const int hn = hi_col ? n : (col_ok ? n - a.G : 0);
+    const int h = g * a.G + hn;
+    uint16_t *outp = (uint16_t *)a.out + ((int64_t)s * a.Hq + h) * D;
+    if (ctx == 0) {
+        if (hi_col) {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) *(i32x2 *)(outp + 16 * t + 4 * j) = i32x2{0, 0};
+        }
+        return;
+    }
+    const int t1 = min(ctx, t0 + per * BS);
+    const int nblk = (t1 - t0 + BS - 1) / BS;  // 1..32
+    if (lane >= nblk || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
+
+    const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)s * a.Hq + h) * D;
+    i32x4 qf[NKC];
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+        qf[c] = col_ok ? ld16(qrow + (4 * c + j) * 8) ^ a.q_xor : i32x4{0, 0, 0, 0};
+    const float cs = a.scale_log2_abs;
+
+    const char *kbase = (const char *)a.k + (int64_t)g * TILE;
+    const char *vbase = (const char *)a.v + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+
+    float m = -INFINITY;
+    float l = 0.f;
+    f32x4 o[NVT];
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    struct Blk {
+        i32x4 k[2][NKC];
+        i32x4 v[NVT];
+    };
+    Blk b0, b1;
+    auto load = [&](Blk &x, int i) {
+        const bool in = i < nblk;
+        const int phys = __builtin_amdgcn_readlane(my_bt, in ? i : 0);
+        const int64_t off = (int64_t)phys * blk_stride;
+        const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+        const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int c = 0; c < NKC; ++c)
+                x.k[hh][c] = bload16<kCachePolicyNT>(rk, ((4 * c + j) * BS + kB * hh + n) * 16);
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) {
+            const int row = (16 * t + n) * BS + 4 * j;
+            const i32x2 lo = bload8<kCachePolicyNT>(rv, row * 2);
+            const i32x2 hi = bload8<kCachePolicyNT>(rv, (row + kB) * 2);
+            x.v[t] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        issue_point();
+    };
+
+    auto step = [&](Blk &x, Blk &y, int i) {
+        f32x4 sc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NKC; ++c) sc[hh] = mfma32<DT>(x.k[hh][c], qf[c], sc[hh]);
+        }
+        load(y, i + 1);
+        const bool tail = i == nblk - 1;
+        int nv = BS;
+        float sv[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[4 * hh + e] = sc[hh][e];
+        if (tail) {
+            nv = t1 - (t0 + i * BS);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (kB * hh + 4 * j + e >= nv) sv[4 * hh + e] = -INFINITY;
+        }
+        float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        bm = xor32_max(xor16_max(bm)) * cs;  // the block has a valid token
+        const bool grow = bm > m + 8.f;
+        if (__any(grow)) {
+            const float mn = grow ? bm : m;
+            const float alpha = fast_exp2(m - mn);
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) o[t] *= alpha;
+            l *= alpha;
+            m = mn;
+        }
+        const float nm = -m;
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(fmaf(sv[e], cs, nm));
+        if (tail) {
+            uint32_t vm[4];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int kb = kB * hh + 4 * j;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (kb + e >= nv) pe[4 * hh + e] = 0.f;
+                vm[2 * hh] = (kb + 0 < nv ? 0x0000ffffu : 0u) | (kb + 1 < nv ? 0xffff0000u : 0u);
+                vm[2 * hh + 1] = (kb + 2 < nv ? 0x0000ffffu : 0u) | (kb + 3 < nv ? 0xffff0000u : 0u);
+            }
+#pragma unroll
+            for (int t = 0; t < NVT; ++t)
+                x.v[t] = i32x4{(int)((uint32_t)x.v[t][0] & vm[0]), (int)((uint32_t)x.v[t][1] & vm[1]),
+                               (int)((uint32_t)x.v[t][2] & vm[2]), (int)((uint32_t)x.v[t][3] & vm[3])};
+        }
+        l += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            hw[w] = pack2<DT>(pe[2 * w], pe[2 * w + 1]);
+            lw[w] = pack2<DT>(pe[2 * w] - elem_lo<DT>(hw[w]), pe[2 * w + 1] - elem_hi<DT>(hw[w]));
+        }
+        const i32x4 phi = {(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+        const i32x4 plo = {(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+        if constexpr (SPLIT) {
+            const i32x4 pw = hi_col ? phi : plo;
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) o[t] = mfma32<DT>(x.v[t], pw, o[t]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < NVT; ++t) {
+                o[t] = mfma32<DT>(x.v[t], phi, o[t]);
+                o[t] = mfma32<DT>(x.v[t], plo, o[t]);
+            }
+        }
+    };
+
+    load(b0, 0);
+    int i = 0;
+    for (; i + 2 <= nblk; i += 2) {
+        step(b0, b1, i);
+        step(b1, b0, i + 1);
+    }
+    if (i < nblk) step(b0, b1, i);
+
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int t = 0; t < NVT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[t][e] += __shfl_down(o[t][e], a.G, 16);
+    }
+    const float lt = xor32_sum(xor16_sum(l));
+    if (!hi_col) return;
+    if (t0 == 0 && t1 == ctx) {
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < NVT; ++t) store4<DT>(outp + 16 * t + 4 * j, o[t], inv);
@@ -620,9 +804,9 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
                 const bool split = 2 * a.G <= 16;
                 if (a.BS == 32) {
                     if (split)
-                        decode_mfma_kernel<DT, D, true, kCachePolicyNT, 32><<<grid, 64, 0, stream>>>(a);
+                        decode_mfma_b32_kernel<DT, D, true><<<grid, 64, 0, stream>>>(a);
                     else
-                        decode_mfma_kernel<DT, D, false, kCachePolicyNT, 32><<<grid, 64, 0, stream>>>(a);
+                        decode_mfma_b32_kernel<DT, D, false><<<grid, 64, 0, stream>>>(a);
                 } else {
                     if (split)
                         decode_mfma_kernel<DT, D, true, kCachePolicyNT, 8><<<grid, 64, 0, stream>>>(a);

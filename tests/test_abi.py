@@ -63,6 +63,7 @@ def _decode(lib, **kw):
     (dict(B=32, dtype=F32), UNSUPPORTED),        # block sizes 8 / 32: matrix-core kernel only
     (dict(B=32, Hq=136, Hkv=4), UNSUPPORTED),    # more than 16 query heads per kv head
     (dict(B=8, P=1024), UNSUPPORTED),            # block size 8: partitions up to 512 tokens
+    (dict(B=32, P=48), UNSUPPORTED),             # block size 32: partitions of whole blocks
     (dict(B=8, NB=300000), UNSUPPORTED),         # block size 8: pools under 2 GiB
     (dict(D=96), UNSUPPORTED),
     (dict(q=None), INVALID),

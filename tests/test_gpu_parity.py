@@ -294,7 +294,7 @@ def test_block_sizes_8_and_32(dev, B, dtype, Hq, Hkv, D):
                                       dtype=dtype)
     log(f"block size {B} {dtype} Hq={Hq} Hkv={Hkv} D={D}")
     g, ref, _ = run_full_case(case, dev, 0, strict=False)
-    for P in (16, 48, 512):
+    for P in ((16, 48, 512) if B == 8 else (32, 64, 96, 1024)):   # B = 32: multiples of 32
         out = g.decode(P)
         check_decode(out, ref, dtype, f"B={B} P={P}")
 
@@ -320,3 +320,8 @@ def test_block_size_limits_are_reported(dev):
     g32 = GpuCase(case32, dev)
     with pytest.raises(pa.PAError):
         g32.decode()        # 32 query heads per kv head run on the VALU kernel: B = 16 only
+    case32.num_heads = 8
+    case32.q = case32.q[:, :8].contiguous()
+    g32 = GpuCase(case32, dev)
+    with pytest.raises(pa.PAError):
+        g32.decode(48)      # block size 32: partitions of whole blocks
