@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--cascade", action="store_true",
                     help="decode with pa_decode_cascade: shared prefix blocks read once per "
                          "group of sequences (groups from the block tables)")
+    ap.add_argument("--append", action="store_true",
+                    help="decode workloads with one new token per sequence: the step is one "
+                         "pa_decode_append call (the decode kernel stores the new tokens)")
     ap.add_argument("--block-size", type=int, default=None,
                     help="tokens per block for the llama3_8b workload (8, 16 or 32)")
     ap.add_argument("--page-kib", type=int, default=2048,
@@ -112,13 +115,14 @@ def raw_bits(t):
     return t.numpy()
 
 
-def measured_traffic(workload, part, root=ROOT):
+def measured_traffic(workload, part, append=False, root=ROOT):
     """HBM bytes per pa_decode launch from the committed counter summary
     (profiles/decode_<workload>_traffic.json: rocprofv3 FETCH_SIZE and
     WRITE_SIZE passes scaled by a plain copy's), or None when no summary exists
     for this workload and partitioning or the kernel sources have changed since
     the counters were taken (the summary records their SHA-256)."""
-    rel = os.path.join("profiles", f"decode_{workload}_traffic.json")
+    rel = os.path.join("profiles",
+                       f"decode_{workload}{'_append' if append else ''}_traffic.json")
     path = os.path.join(root, rel)
     if not os.path.exists(path):
         return None, None
@@ -236,8 +240,23 @@ def main():
     L = len(pools)
     stream = torch.cuda.Stream()  # default priority
 
+    # pa_decode_append: one write step of one token per sequence (its last), no copies
+    append = args.append and len(steps) == 1 and steps[0][0] == "write" and \
+        steps[0][1].shape[0] == S
+    if args.append and not append:
+        print("--append takes workloads whose step writes one token per sequence",
+              file=sys.stderr)
+        sys.exit(2)
+
     def enqueue(layer, write=True, decode=True):
         k, v = pools[layer]
+        if append:
+            if write and decode:
+                pa.pa_decode_append(q, steps[0][1], steps[0][2], k, v, bt, cl, case.scale, out,
+                                    partition_tokens=part)
+            elif decode:
+                pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part)
+            return
         if write:
             for st in steps:
                 if st[0] == "copy":
@@ -292,20 +311,27 @@ def main():
         return wall, e0.elapsed_time(e1)
 
     # timed region: exactly `steps` steps
-    wall, _ = timed(args.steps)
+    wall, step_gpu_ms = timed(args.steps)
     ms_per_step = wall * 1e3 / args.steps
     # the kernels alone, per launch: pa_decode (partition + merge kernels) and
-    # the KV writes (plus block copies for copy-on-write)
+    # the KV writes (plus block copies for copy-on-write); with --append the
+    # roofline covers the fused call, which also stores the new tokens
     _, dec_ms = timed(args.steps, write=False)
-    _, wr_ms = timed(args.steps, decode=False)
     dec_avg = dec_ms / args.steps
-    wr_avg = wr_ms / args.steps
+    if append:
+        wr_avg = None
+        app_avg = step_gpu_ms / args.steps
+    else:
+        _, wr_ms = timed(args.steps, decode=False)
+        wr_avg = wr_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline bytes: each physical block counted once (equal to dec_bytes
     # unless blocks are shared; then the logical rate is reported as effective)
-    achieved = uniq_bytes / (dec_avg * 1e-3) / 1e9
+    roof_bytes = uniq_bytes + (step_bytes - dec_bytes if append else 0)
+    roof_avg = app_avg if append else dec_avg
+    achieved = roof_bytes / (roof_avg * 1e-3) / 1e9
     traffic, traffic_src = ((None, None) if args.cascade or B != 16
-                            else measured_traffic(args.workload, part))
+                            else measured_traffic(args.workload, part, append))
 
     # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
     cpu = None
@@ -352,23 +378,28 @@ def main():
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
                    "seed": case.seed, "partition_tokens": part or "auto",
                    "shared_blocks_hint": shared, "cascade": bool(args.cascade),
+                   "append": bool(append),
                    "groups": int(pb.shape[0]), "max_group_size": int(max_group),
                    "layers_rotated": args.layers},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),
         "decode_us": round(dec_avg * 1e3, 2),
-        "decode_entry": "pa_decode_cascade" if args.cascade else "pa_decode",
+        "append_us": round(app_avg * 1e3, 2) if append else None,
+        "decode_entry": ("pa_decode_cascade" if args.cascade
+                         else "pa_decode_append" if append else "pa_decode"),
         "logical_bytes": int(dec_bytes),
         "unique_bytes": int(uniq_bytes),
-        "write_us": round(wr_avg * 1e3, 2),
+        "write_us": round(wr_avg * 1e3, 2) if wr_avg is not None else None,
         "launch": "HIP graph replays, one graph per pass over the rotated layers",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": ("pa_decode_cascade (unit + merge kernels)" if args.cascade
+                                else "pa_decode_append (partition kernel storing the new "
+                                     "tokens + merge kernel)" if append
                                 else "pa_decode (partition + merge kernels)"),
-                     "bytes_per_launch": int(uniq_bytes)},
+                     "bytes_per_launch": int(roof_bytes)},
         "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

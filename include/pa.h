@@ -110,6 +110,28 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
               int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
 
+/*
+ * pa_decode_append -- one decode step in one call: store the newest token of
+ * every sequence, then attend.  For each sequence s with ctx = context_lens[s]
+ * >= 1, token ctx - 1 is the new one: its keys and values k_new[s], v_new[s]
+ * ([num_seqs][num_kv_heads][head_dim], device) go to its slot, block
+ * block_tables[s][(ctx - 1) / 16] at offset (ctx - 1) % 16, exactly as
+ * pa_write_kv would store them, and the output is pa_decode's over the ctx
+ * tokens.  The unit of the decode kernel that reads that block stores the
+ * token and uses it from registers, so there is no separate write kernel.
+ *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム (block
+ *    table, decode equation)]
+ * Preconditions as pa_write_kv and pa_decode (the block of slot ctx - 1 is
+ * the sequence's own: copy-on-write copies come first).  16-bit data, at most
+ * 16 query heads per kv head, block_size 16; PA_ERR_UNSUPPORTED otherwise.
+ * partition_tokens as pa_decode_ex.
+ */
+int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, void *out, int num_seqs, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                     int dtype, int partition_tokens, void *stream);
+
 /* Flags of pa_decode_ex. */
 enum pa_decode_flags {
     /* Hint: physical blocks of this call are read by several sequences

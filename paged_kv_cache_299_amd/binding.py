@@ -37,7 +37,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_cascade", "pa_prefill",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_append", "pa_decode_cascade",
+    "pa_prefill",
     "pa_copy_blocks", "pa_swap_blocks",
     "pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid", "pa_vkv_step",
     "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy", "pa_vkv_write_kv", "pa_vkv_decode",
@@ -92,6 +93,9 @@ def load_library() -> ctypes.CDLL:
                  "pa_vkv_step", "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy",
                  "pa_vkv_write_kv", "pa_vkv_decode"):
         getattr(lib, name).restype = I32
+    lib.pa_decode_append.argtypes = [P, P, P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32,
+                                     I64, I32, I32, P]
+    lib.pa_decode_append.restype = I32
     lib.pa_decode_cascade.argtypes = [P, P, P, P, P, P, P, I32, I32, F32, P, I32, I32, I32, I32,
                                       I32, I32, I64, I32, I32, P]
     lib.pa_decode_cascade.restype = I32
@@ -203,6 +207,37 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                     partition_tokens: int = 0, stream=None) -> None:
+    """Store each sequence's newest token (position context_lens[s] - 1; k_new /
+    v_new [S, Hkv, D]) into its slot and decode, in one call."""
+    NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
+    S = q.shape[0]
+    _need(q.dim() == 3 and q.shape[2] == D and q.shape == out.shape,
+          "q and out must be [S, Hq, D] with the caches' D")
+    _need(tuple(k_new.shape) == (S, Hkv, D) and k_new.shape == v_new.shape,
+          "k_new / v_new must be [S, Hkv, D]")
+    _need(q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == out.dtype,
+          "q, new tokens, caches and out differ in dtype")
+    for t in (q, out, k_new, v_new):
+        _need(t.is_contiguous() and t.device == k_cache.device,
+              "q, out and new tokens must be contiguous on the caches' GPU")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S and block_tables.is_contiguous()
+          and block_tables.device == k_cache.device, "block_tables must be contiguous int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,)
+          and context_lens.is_contiguous() and context_lens.device == k_cache.device,
+          "context_lens must be contiguous int32 [S]")
+    rc = load_library().pa_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), float(scale), _ptr(out), S, q.shape[1], Hkv, D, B,
+        block_tables.shape[1], NB, DTYPE_CODES[q.dtype], int(partition_tokens),
+        _stream_handle(stream, k_cache.device))
+    _check(rc, "pa_decode_append")
 
 
 def pa_decode_cascade(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

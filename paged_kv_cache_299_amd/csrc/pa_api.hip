@@ -293,7 +293,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *block_tables, const int32_t *context_lens, float scale,
                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
-                int partition_tokens, int flags, void *stream, const Contiguous *contig) {
+                int partition_tokens, int flags, void *stream, const Contiguous *contig,
+                const void *k_new, const void *v_new) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -311,6 +312,9 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                     "pa_decode: partition_tokens %d must be 0 or a multiple of 16 in [16, %d]",
                     partition_tokens, kMaxPartition);
     const bool mfma_ok = dtype != PA_F32 && num_heads / num_kv_heads <= 16;
+    if ((k_new || v_new) && !(mfma_ok && block_size == kBlock && !contig))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_append: 16-bit data, at most 16 query heads "
+                    "per kv head and block_size 16 only");
     if (block_size != kBlock && !((block_size == 8 || block_size == 32) && mfma_ok && !contig))
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (16 is built for every case; "
                     "8 and 32 for 16-bit data with at most 16 query heads per kv head)",
@@ -333,8 +337,10 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_blocks_per_seq too large");
     if (num_seqs == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !(block_tables || contig) || !context_lens || !out ||
-        (contig && (!contig->req || !contig->mapped)))
+        (contig && (!contig->req || !contig->mapped)) || (!k_new != !v_new))
         return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer");
+    if ((k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_append: new tokens must be 16-byte aligned");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
         (contig && ((uintptr_t)contig->req & 3u)))
@@ -386,6 +392,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
     a.BS = block_size;
     a.num_units = (int)units;
     a.shared_blocks = (flags & PA_DECODE_SHARED_BLOCKS) != 0;
+    a.k_new = k_new;
+    a.v_new = v_new;
     if (contig) {
         a.bt = nullptr;
         a.req = contig->req;
@@ -422,6 +430,18 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                            num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                            max_blocks_per_seq, num_blocks, dtype, partition_tokens, flags, stream,
                            nullptr);
+}
+
+int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, void *out, int num_seqs, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                     int dtype, int partition_tokens, void *stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_append: null pointer");
+    return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                           num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                           num_blocks, dtype, partition_tokens, 0, stream, nullptr, k_new, v_new);
 }
 
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,

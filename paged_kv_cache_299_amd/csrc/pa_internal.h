@@ -31,6 +31,10 @@ struct DecodeArgs {
     const int *mapped;      // [num_req]
     int req_stride;
     int num_req;
+    // Append (k_new != nullptr): token ctx - 1 of every sequence is new; its
+    // K/V ([S][Hkv][D]) are stored into its slot by the unit that reads it.
+    const void *k_new;
+    const void *v_new;
 };
 
 enum class DecodeKernel { kValu, kMfma };
@@ -106,7 +110,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *block_tables, const int32_t *context_lens, float scale,
                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
-                int partition_tokens, int flags, void *stream, const Contiguous *contig);
+                int partition_tokens, int flags, void *stream, const Contiguous *contig,
+                const void *k_new = nullptr, const void *v_new = nullptr);
 
 // Record the message pa_last_error() returns on this thread; returns status.
 int api_fail(int status, const char *msg);

@@ -123,6 +123,23 @@ def test_python_swap_rejects_pageable_and_mismatched_pools():
         pa.pa_swap_blocks(k, v, k.clone(), v.clone(), m.int())
 
 
+def test_append_argument_checks():
+    lib = pa.load_library()
+    A = ALIGNED
+    args = [A, A, A, A, A, A, A, 0.1, A, 4, 32, 8, 128, 16, 16, 100, BF16, 0, None]
+    assert lib.pa_decode_append(*args[:1], None, *args[2:]) == INVALID            # no k_new
+    a = list(args); a[16] = F32
+    assert lib.pa_decode_append(*a) == UNSUPPORTED                                  # fp32
+    a = list(args); a[13] = 32
+    assert lib.pa_decode_append(*a) == UNSUPPORTED                                  # block 32
+    a = list(args); a[10] = 136; a[11] = 4
+    assert lib.pa_decode_append(*a) == UNSUPPORTED                                  # G = 34
+    a = list(args); a[1] = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.pa_decode_append(*a) == INVALID                                      # misaligned
+    a = list(args); a[9] = 0
+    assert lib.pa_decode_append(*a) == OK                                           # no sequence
+
+
 def _prefill(lib, **kw):
     args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, bt=ALIGNED, ctx=ALIGNED, qs=ALIGNED, scale=0.1,
                 out=ALIGNED, S=4, T=100, MQ=50, Hq=32, Hkv=8, D=128, B=16, MB=16, NB=100,

@@ -325,3 +325,45 @@ def test_block_size_limits_are_reported(dev):
     g32 = GpuCase(case32, dev)
     with pytest.raises(pa.PAError):
         g32.decode(48)      # block size 32: partitions of whole blocks
+
+
+# --------------------------------------------------------------------------
+# pa_decode_append: the newest token stored by the decode kernel itself
+# --------------------------------------------------------------------------
+def _append_run(case, dev, P=0):
+    """pa_decode_append on the case's pools (before its write step); returns
+    (GpuCase with the updated pools, output)."""
+    g = GpuCase(case, dev)
+    st = case.steps[-1]
+    out = torch.full_like(g.q, float("nan"))
+    pa.pa_decode_append(g.q, st.k_new.to(dev), st.v_new.to(dev), g.k, g.v, g.bt, g.cl,
+                        case.scale, out, partition_tokens=P)
+    torch.cuda.synchronize()
+    return g, out.cpu()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (32, 8), (16, 1), (8, 2)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_append_equals_write_then_decode(dev, dtype, Hq, Hkv, D):
+    ctxs = [1, 15, 16, 17, 0, 300, 1025, 33]
+    case = _case(ctxs, Hq, Hkv, D, dtype, seed=Hq + D)
+    log(f"append {dtype} Hq={Hq} Hkv={Hkv} D={D}")
+    kc, vc = oracle_apply_steps(case)
+    ref = oracle_decode(case, kc, vc)
+    for P in (0, 16, 256, 1024):
+        g, out = _append_run(case, dev, P)
+        assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc), f"P={P}: pools differ"
+        check_decode(out, ref, dtype, f"append P={P}")
+        # the same bits as the separate write and decode
+        g2 = GpuCase(case, dev)
+        g2.apply_steps()
+        assert same_bits(out, g2.decode(P)), f"P={P}: append and write + decode differ"
+
+
+def test_decode_append_full_size_llama(dev):
+    case = workloads.llama3_8b()
+    kc, vc = oracle_apply_steps(case)
+    g, out = _append_run(case, dev)
+    assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc)
+    check_decode(out, oracle_decode(case, kc, vc), case.dtype, "append llama3_8b", strict=True)
