@@ -105,6 +105,20 @@ def calibrate_copy(reps=5):
           flush=True)
 
 
+def host_info():
+    """The host's CPU model and logical CPU count (for the oracle baselines)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def raw_bits(t):
     """numpy view of a CPU tensor's element bits (the oracle's input form)."""
     import numpy as np
@@ -310,6 +324,22 @@ def main():
             wall = time.perf_counter() - t0
         return wall, e0.elapsed_time(e1)
 
+    def spread(passes=25, **phase):
+        """p10 / median / p90 of the per-step GPU time over graph replays of
+        one pass over the layers each (events between replays)."""
+        g_all = capture(range(L), **phase)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
+        with torch.cuda.stream(stream):
+            g_all.replay()
+            ev[0].record(stream)
+            for i in range(passes):
+                g_all.replay()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / L for i in range(passes))
+        return {"p10": round(per[len(per) // 10], 2), "median": round(per[len(per) // 2], 2),
+                "p90": round(per[(9 * len(per)) // 10], 2), "passes": passes, "steps_each": L}
+
     # timed region: exactly `steps` steps
     wall, step_gpu_ms = timed(args.steps)
     ms_per_step = wall * 1e3 / args.steps
@@ -324,6 +354,7 @@ def main():
     else:
         _, wr_ms = timed(args.steps, decode=False)
         wr_avg = wr_ms / args.steps
+    dec_spread = spread(write=False)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline bytes: each physical block counted once (equal to dec_bytes
     # unless blocks are shared; then the logical rate is reported as effective)
@@ -353,7 +384,7 @@ def main():
         t_med = statistics.median(times)
         cpu = {"value": round(dec_bytes / t_med / 1e9, 3), "unit": "GB/s",
                "tokens_per_s": round(S / t_med, 2), "seconds": round(t_med, 3),
-               "cores": oracle.num_threads(), "kind": "oracle",
+               "cores": oracle.num_threads(), "kind": "oracle", **host_info(),
                "sample": f"the full workload (all {S} sequences, layer 0), pa_decode only, "
                          f"median of {args.cpu_reps} runs, fp64"}
         del kh, vh
@@ -385,6 +416,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),
         "decode_us": round(dec_avg * 1e3, 2),
+        "decode_us_spread": dec_spread,
         "append_us": round(app_avg * 1e3, 2) if append else None,
         "decode_entry": ("pa_decode_cascade" if args.cascade
                          else "pa_decode_append" if append else "pa_decode"),
@@ -538,7 +570,7 @@ def bench_prefill(args, dev):
             times.append(time.perf_counter() - t)
         t_med = statistics.median(times)
         cpu = {"value": round(sample_flops / t_med / 1e12, 6), "unit": "TFLOP/s",
-               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle",
+               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle", **host_info(),
                "sample": f"{len(rows)} query rows (16 per sequence, all {Hq} heads) of layer 0, "
                          f"each over its causal prefix, median of {args.cpu_reps} runs, fp64"}
         del kh, vh
@@ -698,7 +730,7 @@ def bench_vattention(args, dev):
             times.append(time.perf_counter() - t)
         t_med = statistics.median(times)
         cpu = {"value": round(dec_bytes / t_med / 1e9, 3), "unit": "GB/s",
-               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle",
+               "seconds": round(t_med, 3), "cores": oracle.num_threads(), "kind": "oracle", **host_info(),
                "sample": f"the full batch (all {S} sequences, layer 0's tokens), median of "
                          f"{args.cpu_reps} runs, fp64"}
 
@@ -837,7 +869,7 @@ def bench_swap(args, dev):
             times.append(time.perf_counter() - t)
         t_med = statistics.median(times)
         cpu = {"value": round(moved / t_med / 1e9, 3), "unit": "GB/s", "seconds": round(t_med, 4),
-               "cores": 1, "kind": "oracle",
+               "cores": 1, "kind": "oracle", **host_info(),
                "sample": f"swap-out of the same {n} blocks between host arrays (memcpy per "
                          f"block, K and V), median of {args.cpu_reps} runs"}
 
