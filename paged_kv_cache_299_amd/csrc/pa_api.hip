@@ -585,7 +585,8 @@ int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: max_blocks_per_seq too large");
     const int G = num_heads / num_kv_heads;
     if ((int64_t)max_query_len * G > (int64_t)1 << 30 || num_seqs > 65535 ||
-        pa::prefill_row_tiles(max_query_len, G) > 65535)
+        pa::prefill_row_tiles(max_query_len, G) > 65535 ||
+        pa::prefill_row_tiles(max_query_len, G) * num_seqs * num_kv_heads > INT32_MAX)
         return fail(PA_ERR_UNSUPPORTED, "pa_prefill: %d sequences x %d queries x %d heads per "
                     "kv head exceed the launch grid", num_seqs, max_query_len, G);
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;

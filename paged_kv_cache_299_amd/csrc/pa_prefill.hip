@@ -23,16 +23,18 @@
 //    by more than 8), causal and tail masking only in the iterations that
 //    need it;
 //  * O^T += V^T . P^T on v_mfma_f32_16x16x32 over the 32 keys: the k slots
-//    8j .. 8j+7 of lane group j hold keys 4j .. 4j+3 of the first block and of
-//    the second block, which is exactly what the lane holds of P^T, and the
-//    A operand is two 8-byte reads of the transposed V tiles at the same
-//    keys.  The weights go in as hi + lo 16-bit parts (hi = RNE(p),
-//    lo = RNE(p - hi)), so P keeps about 16 significant bits.
-// K/V go through one set of operand registers (228 VGPRs, two waves per
+//    8j .. 8j+7 of lane group j are keys 8j .. 8j+7, one 16-byte read of the
+//    transposed V tile (half a 16-token row of one block).  Two lane swaps
+//    (v_permlane32_swap, v_permlane16_swap) move the weights from the score
+//    layout to that one.  The weights go in as hi + lo 16-bit parts
+//    (hi = RNE(p), lo = RNE(p - hi)), so P keeps about 16 significant bits.
+// K/V go through one set of operand registers (224 VGPRs, two waves per
 // SIMD): the next K is requested as soon as the scores are in, the next V as
-// soon as the P.V products have read the current one.  Plain (cacheable)
-// loads: the other waves of the workgroup and the other row tiles of the
-// sequence read the same tiles.
+// soon as the P.V products have read the current one.  The address unit
+// costs about the same per load instruction whatever its width, so every
+// operand load is 16 bytes a lane.  Plain (cacheable) loads: the other waves
+// of the workgroup and the other row tiles of the sequence read the same
+// tiles.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -59,9 +61,17 @@ void prefill_mfma_kernel(const PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int j = lane >> 4;
-    const int g = blockIdx.x;
-    const int s = blockIdx.y;
-    const int tile = gridDim.z - 1 - blockIdx.z;  // the longest tiles first
+    // Workgroups start in linear order, dealt round-robin to the eight XCDs,
+    // each with its own L2.  Linear id L takes kv head L % Hkv (so one head
+    // per XCD when Hkv is a multiple of 8), then the tiles of one sequence,
+    // longest first: the workgroups that run together on an XCD read the same
+    // K/V, which stays in that L2 (95% hits against 83% with the tiles of all
+    // sequences interleaved, and 21% less time on 8 prompts of 1-4k tokens).
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int g = L % gridDim.x;
+    const int r = L / gridDim.x;
+    const int s = r / gridDim.z;
+    const int tile = gridDim.z - 1 - (r - s * gridDim.z);
 
     // The sequence's queries and context, clamped so that no access leaves
     // the buffers whatever the device holds.
@@ -125,7 +135,7 @@ void prefill_mfma_kernel(const PrefillArgs a) {
     // whole iteration ahead, took the kernel to 352 registers and one wave
     // per SIMD.)
     i32x4 kk[2][NKC];
-    i32x2 vv[2][NVT];
+    i32x4 vv[NVT];
     // Iteration it reads blocks 2 it and 2 it + 1; a block past the wave's
     // last one gets a zero-range descriptor (zeros, no memory traffic).
     auto tile_off = [&](int it, int b, bool &in) {
@@ -152,16 +162,20 @@ void prefill_mfma_kernel(const PrefillArgs a) {
         }
         issue_point();
     };
+    // V: lane group j reads keys 8 j .. 8 j + 7 of the 32, i.e. half j & 1 of
+    // the 16-token row of block j >> 1: one 16-byte load per 16 dims.  The two
+    // blocks sit anywhere in the pool, so these are global loads with a lane
+    // address; a block past the wave's last one is replaced by the first (a
+    // valid tile whose keys all get weight 0).
     auto load_v = [&](int it) {
+        bool in0, in1;
+        const int64_t off0 = tile_off(it, 0, in0);
+        const int64_t off1 = tile_off(it, 1, in1);
+        const char *vp = vbase + ((j >> 1) && in1 ? off1 : off0) + n * (kB * 2) + (j & 1) * 16;
+        const __attribute__((address_space(1))) i32x4 *gp =
+            (const __attribute__((address_space(1))) i32x4 *)vp;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            bool in;
-            const int64_t off = tile_off(it, b, in);
-            const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
-#pragma unroll
-            for (int t = 0; t < NVT; ++t)
-                vv[b][t] = bload8<kCachePolicyPlain>(rv, ((16 * t + n) * kB + 4 * j) * 2);
-        }
+        for (int t = 0; t < NVT; ++t) vv[t] = gp[t * kB * 2];  // 16 rows of 32 bytes further
         issue_point();
     };
 
@@ -180,16 +194,15 @@ void prefill_mfma_kernel(const PrefillArgs a) {
         // slots at or past ctx (the tail of the sequence's last block) may hold
         // NaN: their V is zeroed, since a zero weight does not cancel a NaN
         if (key0 + 32 > ctx) {
+            const int kb = key0 + 8 * j;
+            uint32_t mk[4];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int kb = key0 + 16 * b + 4 * j;
-                const uint32_t m0 = (kb + 0 < ctx ? 0x0000ffffu : 0u) | (kb + 1 < ctx ? 0xffff0000u : 0u);
-                const uint32_t m1 = (kb + 2 < ctx ? 0x0000ffffu : 0u) | (kb + 3 < ctx ? 0xffff0000u : 0u);
+            for (int w = 0; w < 4; ++w)
+                mk[w] = (kb + 2 * w < ctx ? 0x0000ffffu : 0u) | (kb + 2 * w + 1 < ctx ? 0xffff0000u : 0u);
 #pragma unroll
-                for (int t = 0; t < NVT; ++t)
-                    vv[b][t] = i32x2{(int)((uint32_t)vv[b][t][0] & m0),
-                                     (int)((uint32_t)vv[b][t][1] & m1)};
-            }
+            for (int t = 0; t < NVT; ++t)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vv[t][w] = (int)((uint32_t)vv[t][w] & mk[w]);
         }
         const bool full = key0 + 31 <= p_min;  // no key of the iteration is masked for any row
         uint32_t hi[kRowTiles][4], lo[kRowTiles][4];
@@ -238,9 +251,29 @@ void prefill_mfma_kernel(const PrefillArgs a) {
                                       pe[2 * w + 1] - elem_hi<DT>(hi[rt][w]));
             }
         }
+        // The scores left lane group j with keys 4j .. 4j+3 of each block
+        // (words 0, 1: block 0; words 2, 3: block 1).  Two lane swaps give it
+        // keys 8j .. 8j+7 of the 32, the k slots of its V operand: the upper
+        // half-wave's block-0 words trade with the lower half-wave's block-1
+        // words, then odd lane groups trade with even ones.
+        auto regroup = [](uint32_t (&w)[4]) {
+            const auto r0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(r0[0], r0[1], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(r1[0], r1[1], false, false);
+            w[0] = s0[0];
+            w[1] = s1[0];
+            w[2] = s0[1];
+            w[3] = s1[1];
+        };
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) {
+            regroup(hi[rt]);
+            regroup(lo[rt]);
+        }
 #pragma unroll
         for (int t = 0; t < NVT; ++t) {
-            const i32x4 va = {vv[0][t][0], vv[0][t][1], vv[1][t][0], vv[1][t][1]};
+            const i32x4 va = vv[t];
 #pragma unroll
             for (int rt = 0; rt < kRowTiles; ++rt) {
                 const i32x4 phi = {(int)hi[rt][0], (int)hi[rt][1], (int)hi[rt][2], (int)hi[rt][3]};

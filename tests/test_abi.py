@@ -164,6 +164,7 @@ def _prefill(lib, **kw):
     (dict(D=96), UNSUPPORTED),
     (dict(S=70000), UNSUPPORTED),
     (dict(T=10_000_000, MQ=10_000_000), UNSUPPORTED),
+    (dict(S=65535, T=2_000_000, MQ=2_000_000), UNSUPPORTED),  # workgroup ids overflow int32
     (dict(S=0), OK),
     (dict(T=0, MQ=0), OK),
 ])
