@@ -192,10 +192,13 @@ __device__ __forceinline__ void cascade_unit(const CascadeArgs &a, int r, int ra
             for (int e = 0; e < 4; ++e)
                 if (4 * j + e >= nv) sc[e] = -INFINITY;
         }
-        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        bm = xor32_max(xor16_max(bm)) * cs;
-        const bool grow = bm > m + 8.f;
-        if (__any(grow)) {
+        // The running maximum moves only when a score passes it by more than 8
+        // (log2 units): each lane tests its own scores, and the row maximum
+        // over the lane groups is formed only when some lane is over.
+        const float lm = max4f(sc[0], sc[1], sc[2], sc[3]);
+        if (__any(lm * cs > m + 8.f)) {
+            const float bm = xor32_max(xor16_max(lm)) * cs;
+            const bool grow = bm > m + 8.f;
             const float mn = grow ? bm : m;
             const float alpha = fast_exp2(m - mn);
 #pragma unroll

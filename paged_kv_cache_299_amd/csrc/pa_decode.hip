@@ -289,10 +289,13 @@ void decode_mfma_kernel(const DecodeArgs a) {
             for (int e = 0; e < 4; ++e)
                 if (4 * j + e >= nv) sc[e] = -INFINITY;
         }
-        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        bm = xor32_max(xor16_max(bm)) * cs;  // the block has a valid token
-        const bool grow = bm > m + 8.f;
-        if (__any(grow)) {
+        // The running maximum moves only when a score passes it by more than 8
+        // (log2 units): each lane tests its own scores, and the row maximum
+        // over the lane groups is formed only when some lane is over.
+        const float lm = max4f(sc[0], sc[1], sc[2], sc[3]);
+        if (__any(lm * cs > m + 8.f)) {
+            const float bm = xor32_max(xor16_max(lm)) * cs;  // the block has a valid token
+            const bool grow = bm > m + 8.f;
             const float mn = grow ? bm : m;
             const float alpha = fast_exp2(m - mn);  // 0 on the first step (m = -inf)
 #pragma unroll
@@ -483,11 +486,12 @@ void decode_mfma_b32_kernel(const DecodeArgs a) {
                 for (int e = 0; e < 4; ++e)
                     if (kB * hh + 4 * j + e >= nv) sv[4 * hh + e] = -INFINITY;
         }
-        float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        bm = xor32_max(xor16_max(bm)) * cs;  // the block has a valid token
-        const bool grow = bm > m + 8.f;
-        if (__any(grow)) {
+        // lazy row maximum, as in the 16-token kernel
+        const float lm = __builtin_elementwise_maximum(max4f(sv[0], sv[1], sv[2], sv[3]),
+                                                       max4f(sv[4], sv[5], sv[6], sv[7]));
+        if (__any(lm * cs > m + 8.f)) {
+            const float bm = xor32_max(xor16_max(lm)) * cs;  // the block has a valid token
+            const bool grow = bm > m + 8.f;
             const float mn = grow ? bm : m;
             const float alpha = fast_exp2(m - mn);
 #pragma unroll

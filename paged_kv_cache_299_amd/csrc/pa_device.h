@@ -80,6 +80,12 @@ __device__ __forceinline__ float xor16_max(float v) {
                                                     false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// IEEE maximum of four values: no quieting of operands the compiler cannot
+// prove canonical (matrix-core results), and v_maximum3_f32 takes three at once.
+__device__ __forceinline__ float max4f(float a, float b, float c, float d) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                         __builtin_elementwise_maximum(c, d));
+}
 __device__ __forceinline__ float xor32_max(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                     false);

@@ -220,11 +220,15 @@ void prefill_mfma_kernel(const PrefillArgs a) {
                     for (int e = 0; e < 4; ++e)
                         if (key0 + 16 * b + 4 * j + e > prow[rt]) sv[4 * b + e] = -INFINITY;
             }
-            float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-            bm = xor32_max(xor16_max(bm)) * cs;  // -inf when the row sees none of these keys
-            const bool grow = bm > m[rt] + 8.f;
-            if (__any(grow)) {
+            // The running maximum only moves when a score passes it by more
+            // than 8 (log2 units), so each lane first tests its own 8 scores
+            // and the row's maximum over the four lane groups is formed only
+            // when some lane of the wave is over.
+            const float lm = __builtin_elementwise_maximum(max4f(sv[0], sv[1], sv[2], sv[3]),
+                                                           max4f(sv[4], sv[5], sv[6], sv[7]));
+            if (__any(lm * cs > m[rt] + 8.f)) {
+                const float bm = xor32_max(xor16_max(lm)) * cs;  // -inf: the row sees none of these keys
+                const bool grow = bm > m[rt] + 8.f;
                 const float mn = grow ? bm : m[rt];
                 const float alpha = fast_exp2(m[rt] - mn);  // 0 on a row's first keys
 #pragma unroll
