@@ -28,13 +28,15 @@
 //    (v_permlane32_swap, v_permlane16_swap) move the weights from the score
 //    layout to that one.  The weights go in as hi + lo 16-bit parts
 //    (hi = RNE(p), lo = RNE(p - hi)), so P keeps about 16 significant bits.
-// K/V go through one set of operand registers (224 VGPRs, two waves per
+// K/V go through one set of operand registers (221 VGPRs, two waves per
 // SIMD): the next K is requested as soon as the scores are in, the next V as
 // soon as the P.V products have read the current one.  The address unit
 // costs about the same per load instruction whatever its width, so every
 // operand load is 16 bytes a lane.  Plain (cacheable) loads: the other waves
 // of the workgroup and the other row tiles of the sequence read the same
 // tiles.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -144,13 +146,13 @@ void prefill_mfma_kernel(const PrefillArgs a) {
         const int phys = __builtin_amdgcn_readlane(my_bt, in ? (blk & (kBtChunk - 1)) : 0);
         return (int64_t)phys * blk_stride;
     };
+    auto load_table = [&](int it) {  // the slice of the block table from block 2 it on
+        const int e = 2 * it + lane;
+        int id = e < nblk ? btrow[e] : 0;
+        if (id < 0 || (int64_t)id >= a.NB) id = 0;
+        my_bt = id;
+    };
     auto load_k = [&](int it) {
-        if ((it & (kBtChunk / 2 - 1)) == 0) {  // next slice of the block table
-            const int e = 2 * it + lane;
-            int id = e < nblk ? btrow[e] : 0;
-            if (id < 0 || (int64_t)id >= a.NB) id = 0;
-            my_bt = id;
-        }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             bool in;
@@ -179,7 +181,15 @@ void prefill_mfma_kernel(const PrefillArgs a) {
         issue_point();
     };
 
-    auto step = [&](int it) {
+    // One step: the 32 keys of blocks 2 it, 2 it + 1 for the wave's 32 rows.
+    // FULL steps mask no key for any row (every key precedes every row's
+    // position and the sequence's tail): they have no masking code, and one
+    // rarely taken branch (the rescale) in the middle, so that the compiler
+    // can lay the exponentials and weight packing of one row tile between the
+    // P.V products of the other.
+    auto step = [&](int it, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        if (((it + 1) & (kBtChunk / 2 - 1)) == 0) load_table(it + 1);
         f32x4 sc[kRowTiles][2];
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt)
@@ -191,56 +201,68 @@ void prefill_mfma_kernel(const PrefillArgs a) {
             }
         load_k(it + 1);
         const int key0 = 32 * it;
-        // slots at or past ctx (the tail of the sequence's last block) may hold
-        // NaN: their V is zeroed, since a zero weight does not cancel a NaN
-        if (key0 + 32 > ctx) {
-            const int kb = key0 + 8 * j;
-            uint32_t mk[4];
+        if constexpr (!FULL) {
+            // slots at or past ctx (the tail of the sequence's last block) may
+            // hold NaN: their V is zeroed, since a zero weight does not cancel a NaN
+            if (key0 + 32 > ctx) {
+                const int kb = key0 + 8 * j;
+                uint32_t mk[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                mk[w] = (kb + 2 * w < ctx ? 0x0000ffffu : 0u) | (kb + 2 * w + 1 < ctx ? 0xffff0000u : 0u);
+                for (int w = 0; w < 4; ++w)
+                    mk[w] = (kb + 2 * w < ctx ? 0x0000ffffu : 0u) |
+                            (kb + 2 * w + 1 < ctx ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int t = 0; t < NVT; ++t)
+                for (int t = 0; t < NVT; ++t)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) vv[t][w] = (int)((uint32_t)vv[t][w] & mk[w]);
+                    for (int w = 0; w < 4; ++w) vv[t][w] = (int)((uint32_t)vv[t][w] & mk[w]);
+            }
         }
-        const bool full = key0 + 31 <= p_min;  // no key of the iteration is masked for any row
-        uint32_t hi[kRowTiles][4], lo[kRowTiles][4];
+        // The running maximum only moves when a score passes it by more than 8
+        // (log2 units), so each lane first tests its own 8 scores per row tile,
+        // and a row's maximum over the four lane groups is formed only when
+        // some lane of the wave is over.
+        float sv[kRowTiles][8], lm[kRowTiles];
+        bool over = false;
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt) {
-            float sv[8];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[4 * b + e] = sc[rt][b][e];
-            if (!full) {
+                for (int e = 0; e < 4; ++e) sv[rt][4 * b + e] = sc[rt][b][e];
+            if constexpr (!FULL) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (key0 + 16 * b + 4 * j + e > prow[rt]) sv[4 * b + e] = -INFINITY;
+                        if (key0 + 16 * b + 4 * j + e > prow[rt]) sv[rt][4 * b + e] = -INFINITY;
             }
-            // The running maximum only moves when a score passes it by more
-            // than 8 (log2 units), so each lane first tests its own 8 scores
-            // and the row's maximum over the four lane groups is formed only
-            // when some lane of the wave is over.
-            const float lm = __builtin_elementwise_maximum(max4f(sv[0], sv[1], sv[2], sv[3]),
-                                                           max4f(sv[4], sv[5], sv[6], sv[7]));
-            if (__any(lm * cs > m[rt] + 8.f)) {
-                const float bm = xor32_max(xor16_max(lm)) * cs;  // -inf: the row sees none of these keys
-                const bool grow = bm > m[rt] + 8.f;
-                const float mn = grow ? bm : m[rt];
-                const float alpha = fast_exp2(m[rt] - mn);  // 0 on a row's first keys
+            lm[rt] = __builtin_elementwise_maximum(max4f(sv[rt][0], sv[rt][1], sv[rt][2], sv[rt][3]),
+                                                   max4f(sv[rt][4], sv[rt][5], sv[rt][6], sv[rt][7]));
+            over = over | (lm[rt] * cs > m[rt] + 8.f);
+        }
+        if (__any(over)) {
 #pragma unroll
-                for (int t = 0; t < NVT; ++t) o[rt][t] *= alpha;
-                l[rt] *= alpha;
-                m[rt] = mn;
+            for (int rt = 0; rt < kRowTiles; ++rt) {
+                const float bm = xor32_max(xor16_max(lm[rt])) * cs;  // -inf: the row sees none of these keys
+                const bool grow = bm > m[rt] + 8.f;
+                if (__any(grow)) {
+                    const float mn = grow ? bm : m[rt];
+                    const float alpha = fast_exp2(m[rt] - mn);  // 0 on a row's first keys
+#pragma unroll
+                    for (int t = 0; t < NVT; ++t) o[rt][t] *= alpha;
+                    l[rt] *= alpha;
+                    m[rt] = mn;
+                }
             }
+        }
+        uint32_t hi[kRowTiles][4], lo[kRowTiles][4];
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) {
             const float nm = -m[rt];
             float pe[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(fmaf(sv[e], cs, nm));
-            if (!full) {  // (-inf) * 0 is NaN when the scale is 0
+            for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(fmaf(sv[rt][e], cs, nm));
+            if constexpr (!FULL) {  // (-inf) * 0 is NaN when the scale is 0
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -289,9 +311,14 @@ void prefill_mfma_kernel(const PrefillArgs a) {
         load_v(it + 1);
     };
 
+    load_table(0);
     load_k(0);
     load_v(0);
-    for (int it = 0; it < iters; ++it) step(it);
+    // steps 0 .. nfull - 1 end at or before the wave's first row: key0 + 31 <= p_min
+    const int nfull = min(iters, p_min >= 31 ? (p_min - 31) / 32 + 1 : 0);
+    int it = 0;
+    for (; it < nfull; ++it) step(it, std::true_type{});
+    for (; it < iters; ++it) step(it, std::false_type{});
 
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
