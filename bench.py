@@ -262,8 +262,17 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    def enqueue(layer, write=True, decode=True):
+    # the loads-only ceiling of the decode's access pattern (pa_read_tiles):
+    # the matrix-core configuration of pa_decode only
+    read_ok = (not args.cascade and not append and not shared and B == 16
+               and dt != torch.float32 and Hq // Hkv <= 16)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def enqueue(layer, write=True, decode=True, read=False):
         k, v = pools[layer]
+        if read:
+            pa.pa_read_tiles(k, v, bt, cl, sink, Hq, partition_tokens=part)
+            return
         if append:
             if write and decode:
                 pa.pa_decode_append(q, steps[0][1], steps[0][2], k, v, bt, cl, case.scale, out,
@@ -355,6 +364,10 @@ def main():
         _, wr_ms = timed(args.steps, decode=False)
         wr_avg = wr_ms / args.steps
     dec_spread = spread(write=False)
+    read_us = None
+    if read_ok:
+        _, rd_ms = timed(args.steps, write=False, decode=False, read=True)
+        read_us = rd_ms / args.steps * 1e3
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # roofline bytes: each physical block counted once (equal to dec_bytes
     # unless blocks are shared; then the logical rate is reported as effective)
@@ -433,6 +446,14 @@ def main():
                                 else "pa_decode (partition + merge kernels)"),
                      "bytes_per_launch": int(roof_bytes)},
         "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        # the decode's K/V loads alone (pa_read_tiles: same units, load
+        # instructions and look-ahead, no arithmetic), timed the same way: the
+        # ceiling of this access pattern on this machine, beside the 8 TB/s peak
+        "read_ceiling": None if read_us is None else {
+            "kernel": "pa_read_tiles", "us": round(read_us, 2),
+            "GBps": round(dec_bytes / (read_us * 1e-6) / 1e9, 2),
+            "frac_of_peak": round(dec_bytes / (read_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "decode_frac_of_ceiling": round(read_us / (dec_avg * 1e3), 4)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

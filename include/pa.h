@@ -166,6 +166,26 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int partition_tokens, int flags, void *stream);
 
 /*
+ * pa_read_tiles -- a measurement aid, not part of the attention path: reads
+ * exactly the K/V tiles that pa_decode_ex would read for these arguments, with
+ * the same work units and load instructions, and does nothing else (no
+ * scores, no softmax, no output).  Its time is the ceiling of the decode's
+ * access pattern on the machine at hand; the decode's time over it is the
+ * cost of everything else.  [論文解説: vAttention, 実験結果 › Decode性能:
+ * decode is bound by memory, so the reads alone bound it]
+ *   sink  device int32, 4-byte aligned; written only in the (practically
+ *         impossible) case that the XOR of all loaded words equals a fixed
+ *         constant, which keeps the loads from being optimised away.
+ * Other arguments as pa_decode_ex (q, out, scale and flags are not taken).
+ * The matrix-core configuration only: 16-bit data, at most 16 query heads per
+ * kv head, block_size 16; PA_ERR_UNSUPPORTED otherwise.
+ */
+int pa_read_tiles(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, int32_t *sink, int num_seqs, int num_heads,
+                  int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                  int64_t num_blocks, int dtype, int partition_tokens, void *stream);
+
+/*
  * pa_decode_cascade -- pa_decode for sequences that share prefix blocks,
  * reading each shared block once per group instead of once per sequence.
  * Under parallel sampling (or beam search) the samples of one prompt keep

@@ -37,7 +37,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_append", "pa_decode_cascade",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_read_tiles", "pa_decode_append",
+    "pa_decode_cascade",
     "pa_prefill",
     "pa_copy_blocks", "pa_swap_blocks",
     "pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid", "pa_vkv_step",
@@ -76,6 +77,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.argtypes = [P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I64, I32,
                                  I32, I32, P]
     lib.pa_decode_ex.restype = I32
+    lib.pa_read_tiles.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, I32, I32, P]
+    lib.pa_read_tiles.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
     lib.pa_copy_blocks.restype = I32
     PP, PI64, PD = ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double)
@@ -207,6 +210,26 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_read_tiles(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, sink: torch.Tensor, num_heads: int, stream=None,
+                  partition_tokens: Optional[int] = 0) -> None:
+    """Measurement aid: the K/V reads of pa_decode for these arguments, nothing else."""
+    NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
+    S = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    _need(sink.dtype == torch.int32 and sink.numel() >= 1, "sink must be an int32 tensor")
+    for t in (block_tables, context_lens, sink):
+        _need(t.is_contiguous() and t.device == k_cache.device, "inputs must be contiguous, same GPU")
+    rc = load_library().pa_read_tiles(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                      _ptr(context_lens), _ptr(sink), S, int(num_heads), Hkv, D,
+                                      B, block_tables.shape[1], NB, DTYPE_CODES[k_cache.dtype],
+                                      int(partition_tokens or 0),
+                                      _stream_handle(stream, k_cache.device))
+    _check(rc, "pa_read_tiles")
 
 
 def pa_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -294,7 +294,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
                 int partition_tokens, int flags, void *stream, const Contiguous *contig,
-                const void *k_new, const void *v_new) {
+                const void *k_new, const void *v_new, int *read_sink) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -404,6 +404,11 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         a.req_stride = contig->req_stride;
         a.num_req = contig->num_req;
     }
+    if (read_sink) {  // pa_read_tiles: the partition kernel's loads alone
+        hipError_t err = pa::launch_read_tiles(a, head_dim, read_sink, (hipStream_t)stream);
+        if (err != hipSuccess) return hip_fail(err, "pa_read_tiles launch");
+        return PA_OK;
+    }
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
@@ -445,6 +450,23 @@ int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *
     return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
                            num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                            num_blocks, dtype, partition_tokens, 0, stream, nullptr, k_new, v_new);
+}
+
+int pa_read_tiles(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, int32_t *sink, int num_seqs, int num_heads,
+                  int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                  int64_t num_blocks, int dtype, int partition_tokens, void *stream) {
+    if (dtype == PA_F32 || (num_kv_heads > 0 && num_heads / num_kv_heads > 16) ||
+        block_size != kBlock)
+        return fail(PA_ERR_UNSUPPORTED, "pa_read_tiles: the matrix-core decode configuration "
+                    "only (16-bit data, at most 16 query heads per kv head, block_size 16)");
+    if (num_seqs > 0 && (!sink || ((uintptr_t)sink & 3u)))
+        return fail(PA_ERR_INVALID_ARG, "pa_read_tiles: sink must be a 4-byte aligned pointer");
+    // q and out are not touched: the K pool stands in for them in the checks
+    return pa::decode_impl(k_cache, k_cache, v_cache, block_tables, context_lens, 1.f,
+                           (void *)k_cache, num_seqs, num_heads, num_kv_heads, head_dim,
+                           block_size, max_blocks_per_seq, num_blocks, dtype, partition_tokens, 0,
+                           stream, nullptr, nullptr, nullptr, sink);
 }
 
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -770,6 +770,82 @@ void decode_valu_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Loads only, for measurement: the K/V tiles decode_mfma_kernel reads, with
+// its work units, its load instructions (16-byte K runs, 8-byte V pieces,
+// nontemporal) and one block requested ahead, folded into an XOR so that no
+// load can be dropped, and nothing else.  Its time is what the decode would
+// take if the reduction cost nothing: the ceiling of this access pattern on
+// the machine at hand.  (The fold is stored only if it equals a constant, so
+// the kernel writes nothing in practice.)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void read_tiles_kernel(const DecodeArgs a, int *sink) {
+    constexpr int NKC = D / 32;
+    constexpr int NVT = D / 16;
+    constexpr int TILE = D * kB * 2;
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    int s, ctx, r;
+    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
+    if (ctx == 0) return;
+    const int g = r % a.Hkv;
+    const int p = r / a.Hkv;
+    const int per = blocks_per_partition(ctx, a.P);
+    const int t0 = p * per * kB;
+    const int t1 = min(ctx, t0 + per * kB);
+    const int nblk = (t1 - t0 + kB - 1) / kB;
+    int my_bt = table_entry(a, s, p * per + lane);
+    if (lane >= nblk || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
+    const char *kbase = (const char *)a.k + (int64_t)g * TILE;
+    const char *vbase = (const char *)a.v + (int64_t)g * TILE;
+    const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+    struct Blk {
+        i32x4 k[NKC];
+        i32x2 v[NVT];
+    };
+    Blk b0, b1;
+    auto load = [&](Blk &x, int i) {
+        const bool in = i < nblk;
+        const int phys = __builtin_amdgcn_readlane(my_bt, in ? i : 0);
+        const int64_t off = (int64_t)phys * blk_stride;
+        const auto rk = tile_rsrc(kbase + off, in ? TILE : 0);
+        const auto rv = tile_rsrc(vbase + off, in ? TILE : 0);
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) x.k[c] = bload16<kCachePolicyNT>(rk, (64 * c + lane) * 16);
+#pragma unroll
+        for (int t = 0; t < NVT; ++t)
+            x.v[t] = bload8<kCachePolicyNT>(rv, ((16 * t + n) * kB + 4 * j) * 2);
+        issue_point();
+    };
+    int acc = 0;
+    auto step = [&](Blk &x, Blk &y, int i) {
+        load(y, i + 1);
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) acc ^= x.k[c][0] ^ x.k[c][1] ^ x.k[c][2] ^ x.k[c][3];
+#pragma unroll
+        for (int t = 0; t < NVT; ++t) acc ^= x.v[t][0] ^ x.v[t][1];
+    };
+    load(b0, 0);
+    int i = 0;
+    for (; i + 2 <= nblk; i += 2) {
+        step(b0, b1, i);
+        step(b1, b0, i + 1);
+    }
+    if (i < nblk) step(b0, b1, i);
+    if (acc == 0x5eed1e55) *sink = acc;
+}
+
+hipError_t launch_read_tiles(const DecodeArgs &a, int head_dim, int *sink, hipStream_t stream) {
+    if (a.num_units <= 0) return hipSuccess;
+    if (head_dim == 64)
+        read_tiles_kernel<64><<<a.num_units, 64, 0, stream>>>(a, sink);
+    else
+        read_tiles_kernel<128><<<a.num_units, 64, 0, stream>>>(a, sink);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp merge of the partitions of one (sequence, query head) by D/4
 // lanes, four dims each:
 //   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise.

@@ -43,6 +43,10 @@ enum class DecodeKernel { kValu, kMfma };
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, DecodeKernel kind,
                          hipStream_t stream);
 
+// Loads only: the K/V tiles the matrix-core partition kernel would read for
+// these arguments (16-bit data, B = 16), for measuring the access pattern.
+hipError_t launch_read_tiles(const DecodeArgs &a, int head_dim, int *sink, hipStream_t stream);
+
 // Everything one prefill launch needs (16-bit data, B = 16).
 struct PrefillArgs {
     const void *q;          // [T][Hq][D], rows of sequence s at qs[s] .. qs[s+1]-1
@@ -111,7 +115,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
                 int partition_tokens, int flags, void *stream, const Contiguous *contig,
-                const void *k_new = nullptr, const void *v_new = nullptr);
+                const void *k_new = nullptr, const void *v_new = nullptr,
+                int *read_sink = nullptr);
 
 // Record the message pa_last_error() returns on this thread; returns status.
 int api_fail(int status, const char *msg);

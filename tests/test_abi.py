@@ -77,6 +77,25 @@ def test_decode_argument_checks(kw, status):
         assert lib.pa_last_error().decode()
 
 
+def test_read_tiles_argument_checks():
+    lib = pa.load_library()
+    A = ALIGNED
+
+    def call(**kw):
+        a = dict(sink=A, S=4, Hq=32, Hkv=8, D=128, B=16, MB=16, dtype=BF16, P=0)
+        a.update(kw)
+        return lib.pa_read_tiles(A, A, A, A, a["sink"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                 a["B"], a["MB"], 100, a["dtype"], a["P"], None)
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(B=32) == UNSUPPORTED
+    assert call(Hq=136, Hkv=4) == UNSUPPORTED
+    assert call(sink=None) == INVALID
+    assert call(sink=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert call(Hq=30) == INVALID
+    assert call(P=20) == INVALID
+    assert call(S=0) == OK
+
+
 def test_write_and_copy_argument_checks():
     lib = pa.load_library()
     A = ALIGNED

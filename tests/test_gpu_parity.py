@@ -215,6 +215,24 @@ def test_workload_full_size(dev, name):
         run_full_case(case, dev, partition_tokens=0, strict=True)
 
 
+@pytest.mark.parametrize("name", ["llama3_8b", "edge"])
+def test_read_tiles_reads_and_writes_nothing(dev, name):
+    # the measurement aid leaves the pools, tables and lengths as they were
+    log(f"pa_read_tiles {name}")
+    case = (workloads.llama3_8b() if name == "llama3_8b"
+            else _case([0, 1, 17, 300, 1025], 16, 4, 64, torch.float16, seed=31))
+    g = GpuCase(case, dev)
+    k0, v0, bt0, cl0 = g.k.clone(), g.v.clone(), g.bt.clone(), g.cl.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for P in (0, 256):
+        pa.pa_read_tiles(g.k, g.v, g.bt, g.cl, sink, case.num_heads, partition_tokens=P)
+    torch.cuda.synchronize()
+    assert torch.equal(g.k.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(g.v.view(torch.int16), v0.view(torch.int16))
+    assert torch.equal(g.bt, bt0) and torch.equal(g.cl, cl0)
+    assert sink.item() in (0, 0x5eed1e55)
+
+
 # --------------------------------------------------------------------------
 # unit search over many sequences (the kernels find their unit from the
 # context lengths 64 sequences at a time), the sign of the scale, and replays
