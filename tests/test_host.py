@@ -172,3 +172,32 @@ def test_shares_blocks_reads_only_the_used_part_of_the_tables():
     assert shares_blocks(ps.block_tables, ps.context_lens, 16)
     ll = workloads.CASES["llama3_8b"](fill=False)
     assert not shares_blocks(ll.block_tables, ll.context_lens, 16)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The build measures one GPU: --gpus N > 1 stops with a message, before
+    anything touches a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout.strip() == ""
+
+
+def test_bench_decode_bytes_follow_the_per_token_closed_form():
+    """Algorithmic bytes of one decode: 2 * Hkv * D * e per token (K and V),
+    plus q in, out, the used table entries and the lengths.  At the
+    Llama-3-8B shape a token costs 2 * 8 * 128 * 2 = 4,096 bytes."""
+    import bench
+    ctx = [1, 16, 17, 4096]
+    S, Hq, Hkv, D, B, e = len(ctx), 32, 8, 128, 16, 2
+    got = bench.decode_bytes(ctx, S, Hq, Hkv, D, B, e)
+    tokens = sum(ctx)
+    blocks = 1 + 1 + 2 + 256
+    assert got == 4096 * tokens + 2 * S * Hq * D * e + 4 * blocks + 4 * S
+    # no block shared: the unique-block count equals the logical one
+    tables = np.arange(S * 256, dtype=np.int32).reshape(S, 256)
+    assert bench.unique_decode_bytes(tables, ctx, S, Hq, Hkv, D, B, e) == got
