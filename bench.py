@@ -129,12 +129,13 @@ def raw_bits(t):
     return t.numpy()
 
 
-def measured_traffic(workload, part, append=False, root=ROOT):
+def measured_traffic(workload, part, append=False, root=ROOT, planned=False):
     """HBM bytes per pa_decode launch from the committed counter summary
     (profiles/decode_<workload>_traffic.json: rocprofv3 FETCH_SIZE and
     WRITE_SIZE passes scaled by a plain copy's), or None when no summary exists
-    for this workload and partitioning or the kernel sources have changed since
-    the counters were taken (the summary records their SHA-256)."""
+    for this workload and partitioning (a fixed length, "auto", or "plan" for
+    pa_decode_plan's choice) or the kernel sources have changed since the
+    counters were taken (the summary records their SHA-256)."""
     rel = os.path.join("profiles",
                        f"decode_{workload}{'_append' if append else ''}_traffic.json")
     path = os.path.join(root, rel)
@@ -142,7 +143,8 @@ def measured_traffic(workload, part, append=False, root=ROOT):
         return None, None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("workload") != workload or rec.get("partition_tokens") != (part or "auto"):
+    label = "plan" if planned else (part or "auto")
+    if rec.get("workload") != workload or rec.get("partition_tokens") != label:
         return None, rel
     for src, digest in rec["sources_sha256"].items():
         with open(os.path.join(root, src), "rb") as f:
@@ -215,6 +217,12 @@ def main():
     NB, dt = case.num_blocks, case.dtype
     e = ELEM_BYTES[dt]
     part = args.partition if args.partition is not None else (case.partition_tokens or 0)
+    # no length given: plan it from the batch's context lengths on the host, as
+    # the scheduler that built the batch would (pa_decode_plan; 0 = automatic)
+    planned = False
+    if args.partition is None and not case.partition_tokens and not args.cascade:
+        part = pa.pa_decode_plan(case.context_lens, Hq, Hkv, B, case.max_blocks, dt)
+        planned = part > 0
     k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
     gen = torch.Generator(device=dev)
     pools = []
@@ -375,7 +383,8 @@ def main():
     roof_avg = app_avg if append else dec_avg
     achieved = roof_bytes / (roof_avg * 1e-3) / 1e9
     traffic, traffic_src = ((None, None) if args.cascade or B != 16
-                            else measured_traffic(args.workload, part, append))
+                            else measured_traffic(args.workload, part, append,
+                                                  planned=planned))
 
     # CPU baseline: the oracle on layer 0's pools after the steps, same inputs
     cpu = None
@@ -421,6 +430,7 @@ def main():
                    "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "num_blocks": NB, "context_tokens": int(sum(ctx)),
                    "seed": case.seed, "partition_tokens": part or "auto",
+                   "partition_plan": "pa_decode_plan (host context lengths)" if planned else None,
                    "shared_blocks_hint": shared, "cascade": bool(args.cascade),
                    "append": bool(append),
                    "groups": int(pb.shape[0]), "max_group_size": int(max_group),

@@ -393,6 +393,31 @@ const char *pa_status_str(int status);
 /* Message for the last failing call on this thread ("" if none). */
 const char *pa_last_error(void);
 
+/*
+ * pa_decode_plan -- host-side planning of the split: the partition length to
+ * pass to pa_decode_ex for this batch, from the context lengths as the
+ * caller's scheduler holds them (host memory; the decode itself reads them
+ * from the device).
+ *   context_lens  host int32 [num_seqs], clamped to [0, max_blocks_per_seq * B]
+ *   *partition_tokens  out: a multiple of 128 in [512, 1024], or 0 where the
+ *                  plan does not apply and the library's automatic choice is
+ *                  the one to take (fp32 data or more than 16 query heads per
+ *                  kv head, block_size other than 16, or num_seqs * kv heads
+ *                  >= 2048, where short partitions keep the machine evenly
+ *                  loaded).
+ * All units of a decode are resident together, so a compute unit runs about
+ * ceil(units / compute units) of them; the plan takes the length that makes
+ * that count times the longest unit (in blocks) smallest, ties to the longer
+ * length.  A partition is still the unit of the online softmax, merged with
+ * log-sum-exp weights.  [論文解説: PagedAttention, 技術的詳細 ›
+ * PagedAttentionアルゴリズム, online softmax; 論文解説: vAttention, 背景と動機:
+ * the host prepares the block tables of each decode step]
+ * Returns PA_OK, or PA_ERR_INVALID_ARG for bad sizes, dtype or null pointers.
+ * Touches no device memory; queries the current device's compute-unit count.
+ */
+int pa_decode_plan(const int32_t *context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                   int block_size, int max_blocks_per_seq, int dtype, int *partition_tokens);
+
 /* Bytes of workspace pa_decode_ex would use for these sizes (0 = none). */
 int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,
                                   int max_blocks_per_seq, int partition_tokens);

@@ -44,7 +44,8 @@ EXPORTS = (
     "pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid", "pa_vkv_step",
     "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy", "pa_vkv_write_kv", "pa_vkv_decode",
     "pa_status_str",
-    "pa_last_error", "pa_decode_workspace_bytes", "pa_release_workspaces", "pa_version",
+    "pa_last_error", "pa_decode_plan", "pa_decode_workspace_bytes", "pa_release_workspaces",
+    "pa_version",
 )
 
 
@@ -111,6 +112,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_status_str.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_decode_plan.argtypes = [P, I32, I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
+    lib.pa_decode_plan.restype = I32
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = I64
     lib.pa_release_workspaces.argtypes = []
@@ -210,6 +213,21 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                      _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_decode_plan(context_lens, num_heads: int, num_kv_heads: int, block_size: int,
+                   max_blocks_per_seq: int, dtype: torch.dtype) -> int:
+    """Partition length for pa_decode from host-side context lengths (0: the
+    library's automatic choice)."""
+    cl = torch.as_tensor(context_lens, dtype=torch.int32).cpu().contiguous()
+    _need(cl.dim() == 1, "context_lens must be one-dimensional")
+    out = ctypes.c_int(0)
+    rc = load_library().pa_decode_plan(ctypes.c_void_p(cl.data_ptr()), cl.shape[0],
+                                       int(num_heads), int(num_kv_heads), int(block_size),
+                                       int(max_blocks_per_seq), DTYPE_CODES[dtype],
+                                       ctypes.byref(out))
+    _check(rc, "pa_decode_plan")
+    return int(out.value)
 
 
 def pa_read_tiles(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,

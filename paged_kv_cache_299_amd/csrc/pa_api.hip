@@ -4,6 +4,7 @@
 // from host-known sizes only (context lengths stay on the device), make sure
 // the split workspace exists, and enqueue the kernels on the caller's stream.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -154,6 +155,28 @@ int auto_partition(bool mfma, int64_t rows, int max_tokens) {
     return 256;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    cache[dev] = cus;
+    return cus;
+}
+
 int64_t num_partitions(int max_tokens, int P) {
     int64_t np = ((int64_t)max_tokens + P - 1) / P;
     return np < 1 ? 1 : np;
@@ -267,6 +290,44 @@ int pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_
                                             (const int64_t *)d[4], num_pairs, num_src_blocks,
                                             num_dst_blocks, block_bytes, (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(err, "pa_swap_blocks launch");
+    return PA_OK;
+}
+
+int pa_decode_plan(const int32_t *context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                   int block_size, int max_blocks_per_seq, int dtype, int *partition_tokens) {
+    if (!partition_tokens) return fail(PA_ERR_INVALID_ARG, "pa_decode_plan: null output");
+    *partition_tokens = 0;
+    if (elem_bytes(dtype) == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode_plan: unknown dtype");
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || block_size <= 0 ||
+        max_blocks_per_seq < 0 || num_heads % num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_plan: bad sizes");
+    if (num_seqs > 0 && !context_lens)
+        return fail(PA_ERR_INVALID_ARG, "pa_decode_plan: null context_lens");
+    const bool mfma = dtype != PA_F32 && num_heads / num_kv_heads <= 16;
+    const int64_t rows = (int64_t)num_seqs * num_kv_heads;
+    // where the plan does not apply, 0: the library's automatic choice
+    if (num_seqs == 0 || !mfma || block_size != kBlock || rows >= 2048) return PA_OK;
+    // Every unit of the split is resident at once, so each compute unit runs
+    // about ceil(units / CUs) of them and the step lasts about as long as
+    // that many of the longest; take the length that makes this product
+    // smallest (ties: the longer partitions, fewer partials to merge).
+    const int64_t cus = device_cus();
+    const int64_t cap = (int64_t)max_blocks_per_seq * kBlock;
+    int best = 0;
+    int64_t best_cost = INT64_MAX;
+    for (int P = 512; P <= kMaxPartition; P += 128) {
+        int64_t units = 0, longest = 0;
+        for (int s = 0; s < num_seqs; ++s) {
+            const int64_t c = std::min<int64_t>(std::max<int32_t>(context_lens[s], 0), cap);
+            const int64_t n = c > P ? (c + P - 1) / P : 1;
+            const int64_t nb = (c + kBlock - 1) / kBlock;
+            units += n * num_kv_heads;
+            longest = std::max(longest, (nb + n - 1) / n);
+        }
+        const int64_t cost = (units + cus - 1) / cus * longest;
+        if (cost <= best_cost) best_cost = cost, best = P;
+    }
+    *partition_tokens = best;
     return PA_OK;
 }
 

@@ -96,6 +96,38 @@ def test_read_tiles_argument_checks():
     assert call(S=0) == OK
 
 
+def test_decode_plan_checks_and_choices():
+    """pa_decode_plan: argument checks, 0 where the plan does not apply, and
+    the partition length that minimises ceil(units / CUs) * longest unit
+    (256 compute units where no GPU is visible), ties to the longer length."""
+    lib = pa.load_library()
+    out = ctypes.c_int(-1)
+
+    def plan(ctx, Hq=32, Hkv=8, B=16, MB=256, dtype=BF16, ptr=True):
+        arr = (ctypes.c_int32 * max(1, len(ctx)))(*ctx)
+        rc = lib.pa_decode_plan(arr if len(ctx) else None, len(ctx), Hq, Hkv, B, MB, dtype,
+                                ctypes.byref(out) if ptr else None)
+        return rc, out.value
+    assert plan([100], ptr=False)[0] == INVALID
+    assert plan([100], dtype=7)[0] == INVALID
+    assert plan([100], Hq=30)[0] == INVALID
+    assert plan([]) == (OK, 0)
+    assert plan([100], dtype=F32) == (OK, 0)                # VALU kernel: automatic
+    assert plan([100], Hq=136, Hkv=4) == (OK, 0)
+    assert plan([100], B=32) == (OK, 0)
+    assert plan([100] * 256) == (OK, 0)                      # 2048 rows: automatic
+    # 32 sequences of 4096 tokens: n partitions cost n * ceil(256 / n) blocks,
+    # 256 at P = 512 and 1024 (the longer wins the tie), more in between
+    assert plan([4096] * 32) == (OK, 1024)
+    # short contexts: one unit each at every length
+    assert plan([100] * 32) == (OK, 1024)
+    # 1,100 tokens (69 blocks): 3 units of 23 blocks at P = 512, cost 3 * 23 = 69;
+    # 2 units of 35 blocks at 640..1024, cost 2 * 35 = 70
+    assert plan([1100] * 32) == (OK, 512)
+    # context lengths beyond the table are clamped (64 blocks = 1024 tokens)
+    assert plan([100000] * 32, MB=64) == plan([1024] * 32, MB=64)
+
+
 def test_write_and_copy_argument_checks():
     lib = pa.load_library()
     A = ALIGNED
