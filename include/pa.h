@@ -203,7 +203,7 @@ int pa_read_tiles(const void *k_cache, const void *v_cache, const int32_t *block
  *                   (prefix_blocks[i] * 16 <= context_lens[s]); 0 = nothing
  *                   shared
  *   max_group_size  host bound on the members of a group (sizes the launch)
- *   partition_tokens  0 (256) or a multiple of 16 in [16, 1024]: shared
+ *   partition_tokens  0 (1024) or a multiple of 16 in [16, 1024]: shared
  *                   prefixes and private suffixes are cut into runs of at
  *                   most that many tokens
  * The result is the attention pa_decode computes, up to rounding: the shared

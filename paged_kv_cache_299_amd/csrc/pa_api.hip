@@ -588,7 +588,9 @@ int pa_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
                     "pa_decode_cascade: data pointers must be 16-byte aligned");
 
     const int G = num_heads / num_kv_heads;
-    const int P = partition_tokens > 0 ? partition_tokens : 256;
+    // default: the longest partitions (fewest partials to merge; parallel
+    // sampling 108 us at 1024 against 117 at 256, 113 at 512)
+    const int P = partition_tokens > 0 ? partition_tokens : kMaxPartition;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * kBlock;
     const int64_t np = max_tokens > 0 ? (max_tokens + P - 1) / P : 1;
     const int64_t tiles = ((int64_t)max_group_size * G + 15) / 16;
