@@ -92,7 +92,7 @@ def test_split_and_single_pass_agree_and_are_deterministic(dev):
     kc, vc = oracle_apply_steps(case)
     ref = oracle_decode(case, kc, vc)
     outs = {}
-    for P in (16, 32, 128, 256, 512, 1024):
+    for P in (16, 32, 128, 256, 512, 640, 768, 896, 1024):  # 640..896: pa_decode_plan's
         outs[P] = g.decode(P).clone()
         check_decode(outs[P], ref, case.dtype, f"P={P}")
         again = g.decode(P)
