@@ -402,13 +402,13 @@ const char *pa_last_error(void);
  *   *partition_tokens  out: a multiple of 128 in [512, 1024], or 0 where the
  *                  plan does not apply and the library's automatic choice is
  *                  the one to take (fp32 data or more than 16 query heads per
- *                  kv head, block_size other than 16, or num_seqs * kv heads
- *                  >= 2048, where short partitions keep the machine evenly
- *                  loaded).
+ *                  kv head, block_size other than 16 and 32, or num_seqs * kv
+ *                  heads >= 2048, where short partitions keep the machine
+ *                  evenly loaded).
  * All units of a decode are resident together, so a compute unit runs about
  * ceil(units / compute units) of them; the plan takes the length that makes
- * that count times the longest unit (in blocks) smallest, ties to the longer
- * length.  A partition is still the unit of the online softmax, merged with
+ * that count times the longest unit (in blocks of block_size tokens)
+ * smallest, ties to the longer length.  A partition is still the unit of the online softmax, merged with
  * log-sum-exp weights.  [論文解説: PagedAttention, 技術的詳細 ›
  * PagedAttentionアルゴリズム, online softmax; 論文解説: vAttention, 背景と動機:
  * the host prepares the block tables of each decode step]

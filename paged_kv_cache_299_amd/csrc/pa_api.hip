@@ -306,13 +306,14 @@ int pa_decode_plan(const int32_t *context_lens, int num_seqs, int num_heads, int
     const bool mfma = dtype != PA_F32 && num_heads / num_kv_heads <= 16;
     const int64_t rows = (int64_t)num_seqs * num_kv_heads;
     // where the plan does not apply, 0: the library's automatic choice
-    if (num_seqs == 0 || !mfma || block_size != kBlock || rows >= 2048) return PA_OK;
+    if (num_seqs == 0 || !mfma || (block_size != kBlock && block_size != 32) || rows >= 2048)
+        return PA_OK;
     // Every unit of the split is resident at once, so each compute unit runs
     // about ceil(units / CUs) of them and the step lasts about as long as
     // that many of the longest; take the length that makes this product
     // smallest (ties: the longer partitions, fewer partials to merge).
     const int64_t cus = device_cus();
-    const int64_t cap = (int64_t)max_blocks_per_seq * kBlock;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
     int best = 0;
     int64_t best_cost = INT64_MAX;
     for (int P = 512; P <= kMaxPartition; P += 128) {
@@ -320,7 +321,7 @@ int pa_decode_plan(const int32_t *context_lens, int num_seqs, int num_heads, int
         for (int s = 0; s < num_seqs; ++s) {
             const int64_t c = std::min<int64_t>(std::max<int32_t>(context_lens[s], 0), cap);
             const int64_t n = c > P ? (c + P - 1) / P : 1;
-            const int64_t nb = (c + kBlock - 1) / kBlock;
+            const int64_t nb = (c + block_size - 1) / block_size;
             units += n * num_kv_heads;
             longest = std::max(longest, (nb + n - 1) / n);
         }

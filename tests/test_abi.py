@@ -114,7 +114,12 @@ def test_decode_plan_checks_and_choices():
     assert plan([]) == (OK, 0)
     assert plan([100], dtype=F32) == (OK, 0)                # VALU kernel: automatic
     assert plan([100], Hq=136, Hkv=4) == (OK, 0)
-    assert plan([100], B=32) == (OK, 0)
+    assert plan([100], B=8) == (OK, 0)
+    # block size 32: units are counted in 32-token blocks (100 tokens: 4 blocks)
+    assert plan([100] * 32, B=32, MB=128) == (OK, 1024)
+    # 1,100 tokens = 35 blocks of 32: 3 units of 12 at 512 (3 * 12 = 36),
+    # 2 of 18 at 640..1024 (2 * 18 = 36): the tie goes to 1024
+    assert plan([1100] * 32, B=32, MB=128) == (OK, 1024)
     assert plan([100] * 256) == (OK, 0)                      # 2048 rows: automatic
     # 32 sequences of 4096 tokens: n partitions cost n * ceil(256 / n) blocks,
     # 256 at P = 512 and 1024 (the longer wins the tie), more in between

@@ -233,14 +233,14 @@ def test_read_tiles_reads_and_writes_nothing(dev, name):
     assert sink.item() in (0, 0x5eed1e55)
 
 
-@pytest.mark.parametrize("seed", [2, 4, 7, 12])
-def test_planned_partition_full_size_llama(dev, seed):
+@pytest.mark.parametrize("seed,B", [(2, 16), (4, 16), (7, 16), (12, 16), (2, 32), (12, 32)])
+def test_planned_partition_full_size_llama(dev, seed, B):
     # the benchmark plans the partition length from the batch's lengths
     # (pa_decode_plan): parity at the length it picks for several draws
-    case = workloads.llama3_8b(seed=seed)
+    case = workloads.llama3_8b(seed=seed, block_size=B)
     P = pa.pa_decode_plan(case.context_lens, case.num_heads, case.num_kv_heads,
                           case.block_size, case.max_blocks, case.dtype)
-    log(f"llama3_8b seed {seed}: planned P = {P}")
+    log(f"llama3_8b seed {seed} B {B}: planned P = {P}")
     assert P in (512, 640, 768, 896, 1024)
     run_full_case(case, dev, partition_tokens=P, strict=True)
 

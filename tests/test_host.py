@@ -227,15 +227,20 @@ def test_block_manager_invariants_under_random_operations(ops, B, nblocks):
     storage = {}   # slot -> token id: what the pool holds
     seen = {}      # sequence -> the token ids it must read, in order
     next_tok = [0]
+    next_seq = [0]
 
     def new_tok():
         next_tok[0] += 1
         return next_tok[0]
 
+    def new_seq():
+        next_seq[0] += 1
+        return next_seq[0]
+
     for op, pick, n in ops:
         live = sorted(seen)
         if op == "alloc":
-            sid = 10_000 + len(seen) + next_tok[0]
+            sid = new_seq()
             try:
                 bm.allocate(sid, n)
             except Exhausted:
@@ -247,8 +252,7 @@ def test_block_manager_invariants_under_random_operations(ops, B, nblocks):
             continue
         elif op == "fork":
             parent = live[pick % len(live)]
-            child = 20_000 + next_tok[0]
-            new_tok()
+            child = new_seq()
             bm.fork(parent, child)
             seen[child] = list(seen[parent])
         elif op == "append":
