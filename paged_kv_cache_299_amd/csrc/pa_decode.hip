@@ -846,23 +846,51 @@ hipError_t launch_read_tiles(const DecodeArgs &a, int head_dim, int *sink, hipSt
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one (sequence, query head) by D/4
-// lanes, four dims each:
-//   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise.
-// The partition count follows from the context length; the results of the
-// first kSpec partitions are requested together with it (all NP partition
-// slots exist in the workspace, stale ones are never combined), so merging up
-// to kSpec partitions costs one round trip.
+// Log-sum-exp merge of the partitions of one (sequence, query head):
+//   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise,
+// over the partitions q = 0 .. np - 1 in order, np following from the context
+// length; out = o / L.
+//
+// merge_kernel (rows of at most 16 partitions): D/4 lanes per row, four dims
+// each.  The (m, l, o) of the first kSpec = 2 partitions are requested
+// together with the context length; the remaining ones (np - 2 <= 14) follow
+// in blocks of 8 requested at once.  Requesting more partitions ahead of the
+// context length reads the slots of partitions that do not exist for short
+// contexts, and those bytes cost more than the extra round trip: on the
+// Llama-3-8B-shaped step (partitions of 640 tokens, up to 7 per row) the
+// decode took 49.0 us with 8 requested ahead, 48.2 with 4 and 47.6-47.8 with
+// 1, 2 or 3 (steady state, MI355X); 2 lanes per dim pair or 1 dim per lane
+// were slower.
+//
+// merge_wide_kernel (more than 16 partitions per row: long contexts): one
+// workgroup per row; its 256 / (D/4) lane groups take every n-th partition,
+// 8 requests in flight each, and combine their states through LDS in group
+// order.  (With a row per D/4 lanes, the 4-sequence long-context step ran its
+// merge on 32 workgroups, a few dozen dependent round trips each.)
 // ---------------------------------------------------------------------------
-// 128 threads = 4 rows at D = 128: measured 0.7 us faster per decode step than
-// 256 (8 rows, half the compute units idle) or 64 (2 rows).
-constexpr int kMergeThreads = 128;
+constexpr int kMergeThreads = 128;   // 4 rows at D = 128
+constexpr int kMergeWideThreads = 256;
+constexpr int kMergeWideMaxParts = 16;  // rows with more partitions take the wide merge
+
+struct LseState {
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // fold in a partition (m_q finite: every partition has a token)
+    __device__ __forceinline__ void add(float mq, float lq, const f32x4 &oq) {
+        const float Mn = fmaxf(M, mq);
+        const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
+        L = L * ca + lq * cb;
+        acc = acc * ca + oq * cb;
+        M = Mn;
+    }
+};
 
 template <int DT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a) {
     constexpr int LPR = D / 4;                // lanes per row
     constexpr int RPB = kMergeThreads / LPR;  // rows per workgroup
-    constexpr int kSpec = 8;
+    constexpr int kSpec = 2;
+    constexpr int kRest = kMergeWideMaxParts - kSpec;
     const int tid = threadIdx.x;
     const int row = blockIdx.x * RPB + tid / LPR;  // s * Hq + h
     const int d0 = (tid % LPR) * 4;
@@ -882,22 +910,74 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a
     const int ctx = seq_ctx(a, s);
     const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
     if (np <= 1) return;  // written by the partition kernel
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto add = [&](float mq, float lq, const f32x4 &oq) {
-        const float Mn = fmaxf(M, mq);  // m_q is finite: every partition has a token
-        const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
-        L = L * ca + lq * cb;
-        acc = acc * ca + oq * cb;
-        M = Mn;
-    };
+    LseState st;
 #pragma unroll
     for (int q = 0; q < kSpec; ++q)
-        if (q < np) add(ml[q].x, ml[q].y, ov[q]);
-#pragma unroll 4
-    for (int q = kSpec; q < np; ++q)
-        add(pml[2 * q], pml[2 * q + 1], *(const f32x4 *)(po + (int64_t)q * D));
-    store4<DT>((char *)a.out + ((int64_t)row * D + d0) * Elem<DT>::bytes, acc, 1.f / L);
+        if (q < np) st.add(ml[q].x, ml[q].y, ov[q]);
+    // the rest (np <= 16: the host takes the wide merge otherwise), in blocks of 8
+#pragma unroll
+    for (int q0 = kSpec; q0 < kSpec + kRest; q0 += 8) {
+        if (q0 >= np) break;
+        float2 m2[8];
+        f32x4 o2[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q0 + q < np) {
+                m2[q] = *(const float2 *)(pml + 2 * (q0 + q));
+                o2[q] = *(const f32x4 *)(po + (int64_t)(q0 + q) * D);
+            }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q0 + q < np) st.add(m2[q].x, m2[q].y, o2[q]);
+    }
+    store4<DT>((char *)a.out + ((int64_t)row * D + d0) * Elem<DT>::bytes, st.acc, 1.f / st.L);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kMergeWideThreads) void merge_wide_kernel(const DecodeArgs a) {
+    constexpr int LPR = D / 4;                       // lanes per group: one row's D outputs
+    constexpr int NGRP = kMergeWideThreads / LPR;    // lane groups
+    constexpr int kIn = 8;                           // partitions in flight per group
+    __shared__ float sm_ml[NGRP][2];
+    __shared__ f32x4 sm_o[NGRP][LPR];
+    const int row = blockIdx.x;  // s * Hq + h
+    const int tid = threadIdx.x;
+    const int grp = tid / LPR, lg = tid % LPR, d0 = lg * 4;
+    const int s = row / a.Hq;
+    const int ctx = seq_ctx(a, s);
+    const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
+    if (np <= 1) return;  // the whole workgroup: written by the partition kernel
+    const float *pml = a.part_ml + (int64_t)row * a.NP * 2;
+    const float *po = a.part_o + (int64_t)row * a.NP * D + d0;
+    // group k folds partitions k, k + NGRP, k + 2 NGRP, ... in order
+    LseState st;
+    for (int q0 = grp; q0 < np; q0 += NGRP * kIn) {
+        float2 m2[kIn];
+        f32x4 o2[kIn];
+#pragma unroll
+        for (int q = 0; q < kIn; ++q) {
+            const int qq = q0 + q * NGRP;
+            if (qq < np) {
+                m2[q] = *(const float2 *)(pml + 2 * qq);
+                o2[q] = *(const f32x4 *)(po + (int64_t)qq * D);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kIn; ++q)
+            if (q0 + q * NGRP < np) st.add(m2[q].x, m2[q].y, o2[q]);
+    }
+    if (lg == 0) {
+        sm_ml[grp][0] = st.M;
+        sm_ml[grp][1] = st.L;
+    }
+    sm_o[grp][lg] = st.acc;
+    __syncthreads();
+    if (grp != 0) return;
+    // groups 0 .. min(np, NGRP) - 1 hold partitions; combine them in order
+    LseState tot;
+    const int ng = np < NGRP ? np : NGRP;
+    for (int k = 0; k < ng; ++k) tot.add(sm_ml[k][0], sm_ml[k][1], sm_o[k][lg]);
+    store4<DT>((char *)a.out + ((int64_t)row * D + d0) * Elem<DT>::bytes, tot.acc, 1.f / tot.L);
 }
 
 // ---------------------------------------------------------------------------
@@ -950,10 +1030,14 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
         if (e != hipSuccess) return e;
     }
     if (a.NP > 1 && a.S > 0) {
-        const int rows_per_block = kMergeThreads / (D / 4);
         const int rows = a.S * a.Hq;
-        merge_kernel<DT, D><<<dim3((rows + rows_per_block - 1) / rows_per_block),
-                               dim3(kMergeThreads), 0, stream>>>(a);
+        if (a.NP > kMergeWideMaxParts) {
+            merge_wide_kernel<DT, D><<<dim3(rows), dim3(kMergeWideThreads), 0, stream>>>(a);
+        } else {
+            const int rows_per_block = kMergeThreads / (D / 4);
+            merge_kernel<DT, D><<<dim3((rows + rows_per_block - 1) / rows_per_block),
+                                   dim3(kMergeThreads), 0, stream>>>(a);
+        }
         return hipGetLastError();
     }
     return hipSuccess;
