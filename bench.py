@@ -296,8 +296,11 @@ def main():
                and dt != torch.float32 and Hq // Hkv <= 16)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def enqueue(layer, write=True, decode=True, read=False):
+    def enqueue(layer, write=True, decode=True, read=False, plain=False):
         k, v = pools[layer]
+        if plain:  # the plain entry point pa_decode: automatic partitions, no hint
+            pa.pa_decode(q, k, v, bt, cl, case.scale, out)
+            return
         if read:
             pa.pa_read_tiles(k, v, bt, cl, sink, Hq, partition_tokens=part)
             return
@@ -394,6 +397,12 @@ def main():
         _, wr_ms = timed(args.steps, decode=False)
         wr_avg = wr_ms / args.steps
     dec_spread = spread(write=False)
+    # plain pa_decode (the library's automatic partition length) beside the
+    # planned length the headline uses, when they differ
+    plain_us = None
+    if part and not args.cascade and not append:
+        _, pl_ms = timed(args.steps, plain=True)
+        plain_us = pl_ms / args.steps * 1e3
     read_us = None
     if read_ok:
         _, rd_ms = timed(args.steps, write=False, decode=False, read=True)
@@ -464,7 +473,9 @@ def main():
         "decode_us_spread": dec_spread,
         "append_us": round(app_avg * 1e3, 2) if append else None,
         "decode_entry": ("pa_decode_cascade" if args.cascade
-                         else "pa_decode_append" if append else "pa_decode"),
+                         else "pa_decode_append" if append
+                         else f"pa_decode_ex (partition_tokens {part})" if part or shared
+                         else "pa_decode"),
         "logical_bytes": int(dec_bytes),
         "unique_bytes": int(uniq_bytes),
         "write_us": round(wr_avg * 1e3, 2) if wr_avg is not None else None,
@@ -478,6 +489,10 @@ def main():
                                 else "pa_decode (partition + merge kernels)"),
                      "bytes_per_launch": int(roof_bytes)},
         "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        "decode_plain": None if plain_us is None else {
+            "entry": "pa_decode (automatic partition length)", "us": round(plain_us, 2),
+            "GBps": round(roof_bytes / (plain_us * 1e-6) / 1e9, 2),
+            "frac_of_peak": round(roof_bytes / (plain_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
         # the decode's K/V loads alone (pa_read_tiles: same units, load
         # instructions and look-ahead, no arithmetic), timed the same way: the
         # ceiling of this access pattern on this machine, beside the 8 TB/s peak

@@ -33,10 +33,14 @@
  * Errors: each call returns a pa_status.  Arguments the host can see (sizes,
  * dtype, null or misaligned pointers) are checked before anything is
  * enqueued; a failing check enqueues nothing.  Values that live on the device
- * (slots, block ids, context lengths) are preconditions: the kernels clamp or
- * skip out-of-range values so that no access leaves the buffers, but the
- * result for such inputs is unspecified.  pa_last_error() gives a message for
- * the last failure on the calling thread.
+ * (slots, block ids, context lengths, block pairs, query starts, groups) are
+ * preconditions, listed with each call: by default the kernels clamp or skip
+ * out-of-range values so that no access leaves the buffers, and the result for
+ * such inputs is unspecified.  With PA_DEBUG on (pa_set_debug below) every
+ * call first checks them on the device, waits for the check, and returns
+ * PA_ERR_INVALID_ARG naming each violated precondition without launching
+ * anything.  pa_last_error() gives a message for the last failure on the
+ * calling thread.
  */
 #ifndef PA_H
 #define PA_H
@@ -100,10 +104,18 @@ int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cac
  * workspace buffer is never freed before pa_release_workspaces, so a HIP graph
  * that captured pa_decode stays valid; the first call on a stream that needs
  * a larger workspace allocates one (hipMalloc), so make that call before
- * capturing.  Results are bit-identical from run to run and do not depend on
- * where the physical blocks sit.
- * Supports block_size 16, head_dim 64 or 128, num_heads a multiple of
- * num_kv_heads; PA_ERR_UNSUPPORTED otherwise.
+ * capturing.  Every call on one stream, and every graph captured on it,
+ * uses that stream's one buffer: such calls and graph replays must not run
+ * at the same time (stream order keeps eager calls apart; two graphs
+ * captured on one stream -- torch.cuda.graph uses one capture stream for
+ * all captures unless it is given one -- must not be replayed concurrently
+ * with each other or with work on that stream).  Give concurrent graphs
+ * their own capture streams.  Results are bit-identical from run to run and
+ * do not depend on where the physical blocks sit.
+ * Supports head_dim 64 or 128 and num_heads a multiple of num_kv_heads;
+ * block_size 16 for every dtype and head ratio, and 8 or 32 for bf16 / fp16
+ * with at most 16 query heads per kv head (block_size 8: pools under 2 GiB);
+ * PA_ERR_UNSUPPORTED otherwise.
  */
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
@@ -118,7 +130,9 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
  * block_tables[s][(ctx - 1) / 16] at offset (ctx - 1) % 16, exactly as
  * pa_write_kv would store them, and the output is pa_decode's over the ctx
  * tokens.  The unit of the decode kernel that reads that block stores the
- * token and uses it from registers, so there is no separate write kernel.
+ * token into the pool and waits for the store before it loads that block, so
+ * there is no separate write kernel.  A new token whose table entry is out of
+ * range ([0, num_blocks)) is not stored.
  *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム (block
  *    table, decode equation)]
  * Preconditions as pa_write_kv and pa_decode (the block of slot ctx - 1 is
@@ -430,6 +444,39 @@ int pa_release_workspaces(void);
 
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int pa_version(void);
+
+/*
+ * pa_set_debug -- switch PA_DEBUG on (nonzero) or off (0) for every later
+ * call in the process; returns the previous setting.  Without a call, the
+ * environment variable PA_DEBUG (set and not "0") decides, read when the
+ * library first needs it.  The pages' convention for an index out of range is
+ * an error raised to the caller (the per-request offset helper raises
+ * ValueError, [論文解説: vAttention, 技術的詳細 ›
+ * リクエスト単位のKVキャッシュインデキシング]); with PA_DEBUG on, each call
+ * checks the preconditions on its device-resident arguments before it
+ * launches anything, and a violation gives PA_ERR_INVALID_ARG (ValueError in
+ * the Python binding) with a message naming it:
+ *   pa_write_kv       slots < num_blocks * B (negative = skip), distinct;
+ *   pa_decode, _ex, _append, pa_read_tiles, pa_prefill, pa_decode_cascade
+ *                     0 <= context_lens[s] <= max_blocks_per_seq * B, and the
+ *                     first ceil(ctx / B) table entries in [0, num_blocks);
+ *   pa_prefill        query_start from 0 to num_tokens, non-decreasing, each
+ *                     chunk at most max_query_len and at most its context;
+ *   pa_decode_cascade groups consecutive from 0 to num_seqs, each of at most
+ *                     max_group_size members, prefix_blocks within the table,
+ *                     every member's context covering them and its entries
+ *                     there equal to the group's first member's;
+ *   pa_copy_blocks    ids in [0, num_blocks), destinations distinct, none a
+ *                     source;
+ *   pa_swap_blocks    ids in range of their pools, destinations distinct, and
+ *                     with one pool pair none a source.
+ * The checks run on the call's stream and are waited for (the call returns
+ * only when they are done), allocate a small scratch buffer (hipMalloc) and
+ * are refused with PA_ERR_INVALID_ARG while the stream is being captured into
+ * a graph.  For finding bad inputs, not for the serving loop.  The virtual-
+ * memory storage calls (pa_vkv_*) are not checked.
+ */
+int pa_set_debug(int on);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,8 @@ Shapes (see layout.py for the pool format):
   pa_write_kv(k_new [T,Hkv,D], v_new [T,Hkv,D], k_cache, v_cache, slot_mapping int64 [T])
   pa_decode(q [S,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
-    (calls pa_decode_ex; shared_blocks sets the PA_DECODE_SHARED_BLOCKS hint)
+    (calls pa_decode, or pa_decode_ex when a partition length or the
+    PA_DECODE_SHARED_BLOCKS hint (shared_blocks) is given)
   pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, group_start int32 [NG+1],
                     prefix_blocks int32 [NG], scale, out, max_group_size=None)
   pa_prefill(q [T,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
@@ -45,7 +46,7 @@ EXPORTS = (
     "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy", "pa_vkv_write_kv", "pa_vkv_decode",
     "pa_status_str",
     "pa_last_error", "pa_decode_plan", "pa_decode_workspace_bytes", "pa_release_workspaces",
-    "pa_version",
+    "pa_version", "pa_set_debug",
 )
 
 
@@ -120,12 +121,20 @@ def load_library() -> ctypes.CDLL:
     lib.pa_release_workspaces.restype = I32
     lib.pa_version.argtypes = []
     lib.pa_version.restype = I32
+    lib.pa_set_debug.argtypes = [I32]
+    lib.pa_set_debug.restype = I32
     _lib = lib
     return lib
 
 
 def pa_status_str(status: int) -> str:
     return load_library().pa_status_str(status).decode()
+
+
+def pa_set_debug(on: bool) -> bool:
+    """PA_DEBUG on or off (device-side precondition checks before every call,
+    ValueError on a violation); returns the previous setting."""
+    return bool(load_library().pa_set_debug(1 if on else 0))
 
 
 def _check(rc: int, what: str) -> None:
@@ -206,12 +215,19 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
           "context_lens must be int32 [S]")
     for t in (q, out, block_tables, context_lens):
         _need(t.is_contiguous() and t.device == k_cache.device, "inputs must be contiguous, same GPU")
-    rc = load_library().pa_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                     _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D,
-                                     B, block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
-                                     int(partition_tokens or 0),
-                                     PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
-                                     _stream_handle(stream, q.device))
+    lib = load_library()
+    if not partition_tokens and not shared_blocks:  # the plain entry point
+        rc = lib.pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                           _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D, B,
+                           block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
+                           _stream_handle(stream, q.device))
+    else:
+        rc = lib.pa_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D, B,
+                              block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
+                              int(partition_tokens or 0),
+                              PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+                              _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
 
 

@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cascade.hip", "pa_cache.hip", "pa_vkv.hip"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cascade.hip", "pa_cache.hip",
+           "pa_vkv.hip", "pa_debug.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

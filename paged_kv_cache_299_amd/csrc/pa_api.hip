@@ -227,6 +227,11 @@ int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cac
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
         ((uintptr_t)slot_mapping & 7u))
         return fail(PA_ERR_INVALID_ARG, "pa_write_kv: data pointers must be 16-byte aligned");
+    if (pa::debug_enabled()) {
+        const int rc = pa::debug_check_slots("pa_write_kv", slot_mapping, num_tokens,
+                                             num_blocks * block_size, (hipStream_t)stream);
+        if (rc != PA_OK) return rc;
+    }
     hipError_t err = pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
                                          num_kv_heads, head_dim, block_size, num_blocks, e,
                                          (hipStream_t)stream);
@@ -252,6 +257,11 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, i
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
     if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_mapping & 7u))
         return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: pools must be 16-byte aligned");
+    if (pa::debug_enabled()) {
+        const int rc = pa::debug_check_pairs("pa_copy_blocks", block_mapping, num_pairs,
+                                             num_blocks, num_blocks, true, (hipStream_t)stream);
+        if (rc != PA_OK) return rc;
+    }
     hipError_t err = pa::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_mapping,
                                             num_pairs, num_blocks, num_blocks, block_bytes,
                                             (hipStream_t)stream);
@@ -284,6 +294,12 @@ int pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_
     const char *names[5] = {"src_k", "src_v", "dst_k", "dst_v", "block_mapping"};
     for (int i = 0; i < 5; ++i) {
         const int rc = device_view(h[i], names[i], &d[i]);
+        if (rc != PA_OK) return rc;
+    }
+    if (pa::debug_enabled()) {
+        const int rc = pa::debug_check_pairs("pa_swap_blocks", (const int64_t *)d[4], num_pairs,
+                                             num_src_blocks, num_dst_blocks,
+                                             d[0] == d[2] || d[1] == d[3], (hipStream_t)stream);
         if (rc != PA_OK) return rc;
     }
     hipError_t err = pa::launch_copy_blocks(d[0], d[1], (void *)d[2], (void *)d[3],
@@ -466,6 +482,13 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         a.req_stride = contig->req_stride;
         a.num_req = contig->num_req;
     }
+    if (pa::debug_enabled() && !contig) {
+        const int rc = pa::debug_check_tables(read_sink ? "pa_read_tiles" : "pa_decode",
+                                              block_tables, context_lens, num_seqs,
+                                              max_blocks_per_seq, block_size, num_blocks,
+                                              (hipStream_t)stream);
+        if (rc != PA_OK) return rc;
+    }
     if (read_sink) {  // pa_read_tiles: the partition kernel's loads alone
         hipError_t err = pa::launch_read_tiles(a, head_dim, read_sink, (hipStream_t)stream);
         if (err != hipSuccess) return hip_fail(err, "pa_read_tiles launch");
@@ -627,6 +650,16 @@ int pa_decode_cascade(const void *q, const void *k_cache, const void *v_cache,
     a.NPP = (int)np;
     a.NPT = (int)(2 * np);
     a.NB = num_blocks;
+    if (pa::debug_enabled()) {
+        int rc = pa::debug_check_tables("pa_decode_cascade", block_tables, context_lens,
+                                        num_seqs, max_blocks_per_seq, block_size, num_blocks,
+                                        (hipStream_t)stream);
+        if (rc == PA_OK)
+            rc = pa::debug_check_groups("pa_decode_cascade", group_start, prefix_blocks,
+                                        block_tables, context_lens, num_groups, num_seqs,
+                                        max_blocks_per_seq, max_group_size, (hipStream_t)stream);
+        if (rc != PA_OK) return rc;
+    }
     void *ws = nullptr;
     const size_t rows = (size_t)num_seqs * num_heads;
     const size_t o_bytes = rows * a.NPT * head_dim * sizeof(float);
@@ -683,6 +716,15 @@ int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
         ((uintptr_t)query_start & 3u))
         return fail(PA_ERR_INVALID_ARG, "pa_prefill: data pointers must be 16-byte aligned");
 
+    if (pa::debug_enabled()) {
+        int rc = pa::debug_check_tables("pa_prefill", block_tables, context_lens, num_seqs,
+                                        max_blocks_per_seq, block_size, num_blocks,
+                                        (hipStream_t)stream);
+        if (rc == PA_OK)
+            rc = pa::debug_check_query_start("pa_prefill", query_start, context_lens, num_seqs,
+                                             num_tokens, max_query_len, (hipStream_t)stream);
+        if (rc != PA_OK) return rc;
+    }
     pa::PrefillArgs a{};
     a.q = q;
     a.k = k_cache;

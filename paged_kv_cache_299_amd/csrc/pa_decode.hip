@@ -188,8 +188,10 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int nblk = (t1 - t0 + kB - 1) / kB;  // 16-token steps, 1..64 (1..32 at BS = 8)
     const int nent = (t1 + BS - 1) / BS - e0;  // table entries of the unit
     // entries past the context are never used; out-of-range ids are clamped so
-    // that no read leaves the pool
-    if (lane >= nent || my_bt < 0 || (int64_t)my_bt >= a.NB) my_bt = 0;
+    // that no read leaves the pool (and the append below stores nothing into
+    // a block whose id was out of range)
+    const int bt_ok = my_bt >= 0 && (int64_t)my_bt < a.NB;
+    if (lane >= nent || !bt_ok) my_bt = 0;
 
     const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)s * a.Hq + h) * D;
     i32x4 qf[NKC];
@@ -213,7 +215,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
     // served), so the loads see them.  (Waiting only before the last block's
     // loads measured slower: 58.6 against 56.0 us on the Llama-3-8B step.)
     if constexpr (APPEND) {
-        if (t1 == ctx) {
+        if (t1 == ctx && __builtin_amdgcn_readlane(bt_ok, nblk - 1)) {
             const int noff = (ctx - 1) & (kB - 1);
             const uint16_t *knp = (const uint16_t *)a.k_new + ((int64_t)s * a.Hkv + g) * D;
             const uint16_t *vnp = (const uint16_t *)a.v_new + ((int64_t)s * a.Hkv + g) * D;

@@ -122,4 +122,21 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
 int api_fail(int status, const char *msg);
 int api_hip_fail(hipError_t e, const char *where);
 
+// PA_DEBUG (pa_debug.hip): checks of the device-resident preconditions, run
+// on the stream and waited for; PA_OK, or PA_ERR_INVALID_ARG naming what is
+// violated.  `who` prefixes the message.
+bool debug_enabled();
+int debug_set(int on);
+int debug_check_tables(const char *who, const int32_t *bt, const int32_t *ctx, int S, int MB,
+                       int B, int64_t NB, hipStream_t stream);
+int debug_check_slots(const char *who, const int64_t *slots, int64_t T, int64_t num_slots,
+                      hipStream_t stream);
+int debug_check_pairs(const char *who, const int64_t *pairs, int64_t n, int64_t src_blocks,
+                      int64_t dst_blocks, bool same_pool, hipStream_t stream);
+int debug_check_query_start(const char *who, const int32_t *qs, const int32_t *ctx, int S, int T,
+                            int max_query_len, hipStream_t stream);
+int debug_check_groups(const char *who, const int32_t *gs, const int32_t *pblk, const int32_t *bt,
+                       const int32_t *ctx, int NG, int S, int MB, int max_group,
+                       hipStream_t stream);
+
 }  // namespace pa

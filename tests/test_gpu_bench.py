@@ -39,3 +39,7 @@ def test_bench_prints_one_complete_json_line():
     assert rc["kernel"] == "pa_read_tiles" and rc["us"] > 0
     # the loads alone cannot take longer than the decode that makes them
     assert rc["us"] <= d["decode_us"] * 1.05
+    # the plain entry point is reported beside the planned partition length
+    plain = d["decode_plain"]
+    assert plain["entry"].startswith("pa_decode ") and plain["us"] > 0
+    assert abs(plain["frac_of_peak"] * 8000.0 - plain["GBps"]) < 1.0

@@ -397,3 +397,58 @@ def test_decode_append_full_size_llama(dev):
     g, out = _append_run(case, dev)
     assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc)
     check_decode(out, oracle_decode(case, kc, vc), case.dtype, "append llama3_8b", strict=True)
+
+
+# --------------------------------------------------------------------------
+# the C entry point pa_decode itself (automatic partitioning), called through
+# ctypes on the full-size Llama-3-8B-shaped batch
+# --------------------------------------------------------------------------
+def test_pa_decode_symbol_full_size_llama(dev):
+    import ctypes
+    case = workloads.llama3_8b()
+    log("pa_decode symbol, llama3_8b")
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    out = torch.full_like(g.q, float("nan"))
+    lib = pa.load_library()
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.pa_decode(P(g.q.data_ptr()), P(g.k.data_ptr()), P(g.v.data_ptr()),
+                       P(g.bt.data_ptr()), P(g.cl.data_ptr()), ctypes.c_float(case.scale),
+                       P(out.data_ptr()), case.num_seqs, case.num_heads, case.num_kv_heads,
+                       case.head_dim, case.block_size, case.max_blocks, case.num_blocks,
+                       pa.DTYPE_CODES[case.dtype], P(stream))
+    assert rc == 0, lib.pa_last_error().decode()
+    torch.cuda.synchronize()
+    kc, vc = oracle_apply_steps(case)
+    check_decode(out.cpu(), oracle_decode(case, kc, vc), case.dtype, "pa_decode llama3_8b",
+                 strict=True)
+
+
+def test_decode_append_skips_out_of_range_entry(dev):
+    """A sequence whose last table entry is out of range gets no store (as
+    pa_write_kv skips a slot outside the pool): every other sequence's new
+    token lands in its slot, and nothing else in the pool changes."""
+    import oracle
+    from helpers import CODE, raw
+    case = _case([17, 40, 33, 1], 8, 2, 128, torch.bfloat16, seed=9)
+    st = case.steps[-1]
+    bad_seq = 1
+    bt = case.block_tables.clone()
+    bt[bad_seq, (40 - 1) // 16] = case.num_blocks + 3
+    slots = st.slot_mapping.clone()
+    slots[bad_seq] = -1
+    kc, vc = oracle.write_kv(raw(st.k_new), raw(st.v_new), raw(case.k_cache), raw(case.v_cache),
+                             slots.numpy(), num_kv_heads=2, head_dim=128, block_size=16, k_x=8,
+                             dtype=CODE[case.dtype])
+    g = GpuCase(case, dev)
+    out = torch.full_like(g.q, float("nan"))
+    pa.pa_decode_append(g.q, st.k_new.to(dev), st.v_new.to(dev), g.k, g.v, bt.to(dev), g.cl,
+                        case.scale, out)
+    torch.cuda.synchronize()
+    assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc), "pool changed beyond the slots"
+    ref = oracle.decode(raw(case.q), kc, vc, case.block_tables.numpy(), case.context_lens.numpy(),
+                        case.scale, num_kv_heads=2, head_dim=128, block_size=16, k_x=8,
+                        dtype=CODE[case.dtype])
+    keep = [s for s in range(case.num_seqs) if s != bad_seq]
+    check_decode(out.cpu()[keep], ref[keep], case.dtype, "append, one bad entry")
