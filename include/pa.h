@@ -180,6 +180,30 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  int partition_tokens, int flags, void *stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode_ex that allocates nothing, for callers that
+ * cannot call hipMalloc: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, same kernels, and the
+ * same bits as pa_decode_ex with the same partition length; the partials of
+ * split contexts go to a static device array of 32 MiB in the library (one
+ * per GPU, held until the process ends) instead of the per-stream workspace.
+ *   Limit: num_seqs * num_heads * ceil(max_blocks_per_seq * B / P) *
+ *   (head_dim + 2) * 4 bytes of partials at most 32 MiB - 256
+ *   (PA_ERR_UNSUPPORTED beyond, before anything is enqueued; e.g. 32
+ *   sequences x 32 heads of up to 131,072 tokens at P = 1024, or 128 of up to
+ *   4,096 at P = 256).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (on different streams, or
+ * graph replays running concurrently) race and give wrong results.  Nothing
+ * in the array needs to start at zero.  With PA_DEBUG on, the checks use the
+ * array too (they still wait for the stream).
+ */
+int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                      int partition_tokens, int flags, void *stream);
+
+/*
  * pa_read_tiles -- a measurement aid, not part of the attention path: reads
  * exactly the K/V tiles that pa_decode_ex would read for these arguments, with
  * the same work units and load instructions, and does nothing else (no

@@ -38,7 +38,8 @@ PA_DECODE_SHARED_BLOCKS = 1
 
 # every symbol include/pa.h declares
 EXPORTS = (
-    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_read_tiles", "pa_decode_append",
+    "pa_write_kv", "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_read_tiles",
+    "pa_decode_append",
     "pa_decode_cascade",
     "pa_prefill",
     "pa_copy_blocks", "pa_swap_blocks",
@@ -79,6 +80,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_ex.argtypes = [P, P, P, P, P, F32, P, I32, I32, I32, I32, I32, I32, I64, I32,
                                  I32, I32, P]
     lib.pa_decode_ex.restype = I32
+    lib.pa_decode_noalloc.argtypes = lib.pa_decode_ex.argtypes
+    lib.pa_decode_noalloc.restype = I32
     lib.pa_read_tiles.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, I32, I32, P]
     lib.pa_read_tiles.restype = I32
     lib.pa_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, I32, P]
@@ -229,6 +232,31 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                               _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
+
+
+def pa_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor, stream=None, partition_tokens: int = 0,
+                      shared_blocks: bool = False) -> None:
+    """pa_decode_ex that allocates nothing: partials in the library's static
+    per-GPU array (calls on one GPU must not overlap in time)."""
+    NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
+    _need(out.shape == q.shape and out.dtype == q.dtype == k_cache.dtype,
+          "out must match q, and q must match the caches' dtype")
+    S, Hq = q.shape[0], q.shape[1]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S, MB]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens must be int32 [S]")
+    for t in (q, out, block_tables, context_lens):
+        _need(t.is_contiguous() and t.device == k_cache.device, "inputs must be contiguous, same GPU")
+    rc = load_library().pa_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(out), S, Hq, Hkv, D, B, block_tables.shape[1], NB,
+        DTYPE_CODES[q.dtype], int(partition_tokens or 0),
+        PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream_handle(stream, q.device))
+    _check(rc, "pa_decode_noalloc")
 
 
 def pa_decode_plan(context_lens, num_heads: int, num_kv_heads: int, block_size: int,

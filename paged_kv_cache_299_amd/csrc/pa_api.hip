@@ -97,6 +97,45 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
     return PA_OK;
 }
 
+// ---- allocation-free decode: the split workspace in a static device array ----
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops, harnesses that forbid hipMalloc): pa_decode_noalloc keeps its
+// partials in this array, one copy per GPU, held until the process ends.
+// Every call on a GPU shares that GPU's copy, so such calls must not overlap
+// in time on one GPU.  In host code `scratch` is a stand-in, not a device
+// address: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // 32 MiB
+constexpr size_t kScratchFlags = 256;                // PA_DEBUG flags word, then partials
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use).
+int scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "pa_decode_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc: device %d (at most %d devices)", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(PA_ERR_HIP, "pa_decode_noalloc: hipGetSymbolAddress: %s",
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
 // The address a kernel uses for p: device memory as it is, pinned host memory
 // (hipHostMalloc; torch's pin_memory) through its device mapping.  Pageable
 // host memory cannot be reached by a kernel: PA_ERR_INVALID_ARG.
@@ -372,7 +411,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
                 int partition_tokens, int flags, void *stream, const Contiguous *contig,
-                const void *k_new, const void *v_new, int *read_sink) {
+                const void *k_new, const void *v_new, int *read_sink, bool no_alloc) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype %d", dtype);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -482,11 +521,24 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         a.req_stride = contig->req_stride;
         a.num_req = contig->num_req;
     }
+    const size_t part_bytes =
+        NP > 1 ? (size_t)num_seqs * num_heads * NP * (head_dim + 2) * sizeof(float) : 0;
+    void *fixed = nullptr;  // pa_decode_noalloc: the static scratch
+    if (no_alloc) {
+        if (part_bytes > kScratchBytes - kScratchFlags)
+            return fail(PA_ERR_UNSUPPORTED,
+                        "pa_decode_noalloc: %zu bytes of partials (%d sequences x %d heads x %lld "
+                        "partitions) exceed the %zu-byte static workspace; use pa_decode",
+                        part_bytes, num_seqs, num_heads, (long long)NP,
+                        kScratchBytes - kScratchFlags);
+        const int rc = scratch_address(&fixed);
+        if (rc != PA_OK) return rc;
+    }
     if (pa::debug_enabled() && !contig) {
         const int rc = pa::debug_check_tables(read_sink ? "pa_read_tiles" : "pa_decode",
                                               block_tables, context_lens, num_seqs,
                                               max_blocks_per_seq, block_size, num_blocks,
-                                              (hipStream_t)stream);
+                                              (hipStream_t)stream, (unsigned *)fixed);
         if (rc != PA_OK) return rc;
     }
     if (read_sink) {  // pa_read_tiles: the partition kernel's loads alone
@@ -497,9 +549,12 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
-        const size_t ml_bytes = (size_t)num_seqs * num_heads * NP * 2 * sizeof(float);
-        int rc = workspace_for((hipStream_t)stream, o_bytes + ml_bytes, &ws);
-        if (rc != PA_OK) return rc;
+        if (fixed) {
+            ws = (char *)fixed + kScratchFlags;
+        } else {
+            const int rc = workspace_for((hipStream_t)stream, part_bytes, &ws);
+            if (rc != PA_OK) return rc;
+        }
         a.part_o = (float *)ws;
         a.part_ml = (float *)((char *)ws + o_bytes);
     }
@@ -523,6 +578,17 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                            num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                            max_blocks_per_seq, num_blocks, dtype, partition_tokens, flags, stream,
                            nullptr);
+}
+
+int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      void *out, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
+                      int partition_tokens, int flags, void *stream) {
+    return pa::decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, num_blocks, dtype, partition_tokens, flags, stream,
+                           nullptr, nullptr, nullptr, nullptr, true);
 }
 
 int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,

@@ -172,13 +172,14 @@ int grid_for(int64_t n) {
 struct Scratch {
     void *p = nullptr;
     size_t bytes = 0;
+    bool owned = true;
     ~Scratch() {
-        if (p) (void)hipFree(p);
+        if (p && owned) (void)hipFree(p);
     }
 };
 
 int begin(const char *who, hipStream_t stream, size_t bitmap_words, Scratch &sc,
-          unsigned **flags, unsigned **bitmaps) {
+          unsigned **flags, unsigned **bitmaps, unsigned *given = nullptr) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(stream, &cs);
     if (e != hipSuccess) return api_hip_fail(e, who);
@@ -188,6 +189,15 @@ int begin(const char *who, hipStream_t stream, size_t bitmap_words, Scratch &sc,
         return api_fail(PA_ERR_INVALID_ARG, m.c_str());
     }
     sc.bytes = (1 + bitmap_words) * sizeof(unsigned);
+    if (given && bitmap_words == 0) {  // the caller's word: nothing to allocate
+        sc.p = given;
+        sc.owned = false;
+        e = hipMemsetAsync(sc.p, 0, sc.bytes, stream);
+        if (e != hipSuccess) return api_hip_fail(e, who);
+        *flags = given;
+        *bitmaps = nullptr;
+        return PA_OK;
+    }
     e = hipMalloc(&sc.p, sc.bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -236,11 +246,11 @@ int debug_set(int on) {
 }
 
 int debug_check_tables(const char *who, const int32_t *bt, const int32_t *ctx, int S, int MB,
-                       int B, int64_t NB, hipStream_t stream) {
+                       int B, int64_t NB, hipStream_t stream, unsigned *flags_buf) {
     if (S <= 0) return PA_OK;
     Scratch sc;
     unsigned *flags, *bm;
-    int rc = begin(who, stream, 0, sc, &flags, &bm);
+    int rc = begin(who, stream, 0, sc, &flags, &bm, flags_buf);
     if (rc != PA_OK) return rc;
     check_tables_kernel<<<grid_for((int64_t)S * (MB > 0 ? MB : 1)), 256, 0, stream>>>(
         bt, ctx, S, MB, B, NB, flags);

@@ -116,7 +116,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
                 int block_size, int max_blocks_per_seq, int64_t num_blocks, int dtype,
                 int partition_tokens, int flags, void *stream, const Contiguous *contig,
                 const void *k_new = nullptr, const void *v_new = nullptr,
-                int *read_sink = nullptr);
+                int *read_sink = nullptr, bool no_alloc = false);
 
 // Record the message pa_last_error() returns on this thread; returns status.
 int api_fail(int status, const char *msg);
@@ -127,8 +127,9 @@ int api_hip_fail(hipError_t e, const char *where);
 // violated.  `who` prefixes the message.
 bool debug_enabled();
 int debug_set(int on);
+// flags_buf: a device word to use instead of allocating one (allocation-free callers)
 int debug_check_tables(const char *who, const int32_t *bt, const int32_t *ctx, int S, int MB,
-                       int B, int64_t NB, hipStream_t stream);
+                       int B, int64_t NB, hipStream_t stream, unsigned *flags_buf = nullptr);
 int debug_check_slots(const char *who, const int64_t *slots, int64_t T, int64_t num_slots,
                       hipStream_t stream);
 int debug_check_pairs(const char *who, const int64_t *pairs, int64_t n, int64_t src_blocks,

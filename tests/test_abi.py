@@ -344,3 +344,19 @@ def test_pa_debug_environment_variable():
                            capture_output=True, text=True, timeout=120)
         assert r.returncode == 0, r.stderr
         assert r.stdout.split() == [str(first), "0", "1"], (env_value, r.stdout)
+
+
+@fake_pointers
+def test_noalloc_rejects_a_workspace_past_its_static_array():
+    """pa_decode_noalloc refuses, before anything else, partials that would
+    not fit its 32 MiB static array; sizes that fit pass the same check."""
+    lib = pa.load_library()
+    A = ALIGNED
+    # 4 sequences x 32 heads x 2^16 partitions of 16 tokens: ~4.4 GB of partials
+    rc = lib.pa_decode_noalloc(A, A, A, A, A, 0.1, A, 4, 32, 8, 128, 16, 65536, 100, BF16, 16,
+                               0, None)
+    assert rc == UNSUPPORTED and "static workspace" in lib.pa_last_error().decode()
+    # the same arguments are fine for pa_decode_ex's size checks: it would
+    # allocate (not called here past its checks: num_seqs = 0 returns first)
+    assert lib.pa_decode_noalloc(A, A, A, A, A, 0.1, A, 0, 32, 8, 128, 16, 65536, 100, BF16, 16,
+                                 0, None) == OK
