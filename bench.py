@@ -38,6 +38,11 @@ WARM_S = 0.1  # untimed GPU work before each timed phase (see warm_graph())
 WORKLOAD_TEXT = {
     "llama3_8b": "Llama-3-8B-shaped GQA decode, one layer: 32 seqs, 32 q / 8 kv heads, D 128, "
                  "B 16, ctx ~ U{128..4096}, pool 12,000 blocks, bf16",
+    "llama3_8b_table128k": "the Llama-3-8B-shaped batch with block tables of 131,072-token "
+                           "capacity (8,192 entries; same lengths U{128..4096}): launch "
+                           "sized by the table, not the work",
+    "many_seqs": "512 sequences of U{128..600} tokens, 32 q / 8 kv heads, D 128, B 16, tables "
+                 "of 40 blocks, bf16: the unit search over 8 rounds of 64 sequences",
     "opt_13b": "OPT-13B-shaped MHA decode, one layer: 64 seqs, 40 heads, D 128, B 16, "
                "ctx lognormal median 512 clipped [16, 2048], pool 10,000 blocks, fp16",
     "parallel_sampling": "parallel sampling: 16 prompts x 8 samples, 32 heads, D 128, B 16, "
@@ -81,6 +86,10 @@ def parse():
     ap.add_argument("--append", action="store_true",
                     help="decode workloads with one new token per sequence: the step is one "
                          "pa_decode_append call (the decode kernel stores the new tokens)")
+    ap.add_argument("--warm-ms", type=float, default=WARM_S * 1e3,
+                    help="untimed GPU work before each timed phase, ms (profiling runs: 0)")
+    ap.add_argument("--force-valu", action="store_true",
+                    help="measurement: the one-head VALU kernel on 16-bit data (PA_DECODE_FORCE_VALU)")
     ap.add_argument("--block-size", type=int, default=None,
                     help="tokens per block for the llama3_8b workload (8, 16 or 32)")
     ap.add_argument("--page-kib", type=int, default=2048,
@@ -105,7 +114,7 @@ def warm_graph(g, stream, seconds=None):
         g.replay()
         torch.cuda.synchronize()
         one = max(time.perf_counter() - t0, 1e-5)
-        for _ in range(max(3, int(seconds / one))):
+        for _ in range(max(3, int(seconds / one)) if seconds > 0 else 1):
             g.replay()
         torch.cuda.synchronize()
 
@@ -196,6 +205,8 @@ def decode_bytes(ctx, S, Hq, Hkv, D, B, e):
 
 def main():
     args = parse()
+    global WARM_S
+    WARM_S = args.warm_ms * 1e-3
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -240,7 +251,8 @@ def main():
     # no length given: plan it from the batch's context lengths on the host, as
     # the scheduler that built the batch would (pa_decode_plan; 0 = automatic)
     planned = False
-    if args.partition is None and not case.partition_tokens and not args.cascade:
+    if args.partition is None and not case.partition_tokens and not args.cascade \
+            and not args.force_valu:
         part = pa.pa_decode_plan(case.context_lens, Hq, Hkv, B, case.max_blocks, dt)
         planned = part > 0
     k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
@@ -293,7 +305,7 @@ def main():
     # the loads-only ceiling of the decode's access pattern (pa_read_tiles):
     # the matrix-core configuration of pa_decode only
     read_ok = (not args.cascade and not append and not shared and B == 16
-               and dt != torch.float32 and Hq // Hkv <= 16)
+               and dt != torch.float32 and Hq // Hkv <= 16 and not args.force_valu)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def enqueue(layer, write=True, decode=True, read=False, plain=False):
@@ -322,7 +334,7 @@ def main():
                                  max_group_size=max_group, partition_tokens=part)
         elif decode:
             pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part,
-                         shared_blocks=shared)
+                         shared_blocks=shared, force_valu=args.force_valu)
 
     # eager warmup on the capture stream (grows the library's workspace for it)
     with torch.cuda.stream(stream):
@@ -400,7 +412,7 @@ def main():
     # plain pa_decode (the library's automatic partition length) beside the
     # planned length the headline uses, when they differ
     plain_us = None
-    if part and not args.cascade and not append:
+    if part and not args.cascade and not append and not args.force_valu:
         _, pl_ms = timed(args.steps, plain=True)
         plain_us = pl_ms / args.steps * 1e3
     read_us = None
@@ -413,7 +425,7 @@ def main():
     roof_bytes = uniq_bytes + (step_bytes - dec_bytes if append else 0)
     roof_avg = app_avg if append else dec_avg
     achieved = roof_bytes / (roof_avg * 1e-3) / 1e9
-    traffic, traffic_src = ((None, None) if args.cascade or B != 16
+    traffic, traffic_src = ((None, None) if args.cascade or B != 16 or args.force_valu
                             else measured_traffic(args.workload, part, append,
                                                   planned=planned))
 
@@ -464,6 +476,7 @@ def main():
                    "partition_plan": "pa_decode_plan (host context lengths)" if planned else None,
                    "shared_blocks_hint": shared, "cascade": bool(args.cascade),
                    "append": bool(append),
+                   "kernel": "valu (PA_DECODE_FORCE_VALU)" if args.force_valu else None,
                    "groups": int(pb.shape[0]), "max_group_size": int(max_group),
                    "layers_rotated": args.layers},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),

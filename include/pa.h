@@ -154,7 +154,12 @@ enum pa_decode_flags {
      * block hit in L2; without the hint they are streamed with nontemporal
      * loads, which is faster when every block is read once.  Results are
      * bit-identical either way. */
-    PA_DECODE_SHARED_BLOCKS = 1
+    PA_DECODE_SHARED_BLOCKS = 1,
+    /* For testing and measurement: run the one-query-head VALU kernel (dot
+     * products and P.V on the vector ALUs) on 16-bit data too, where the
+     * matrix-core kernel would run; same results within the tolerance.
+     * block_size 16 only (PA_ERR_UNSUPPORTED otherwise). */
+    PA_DECODE_FORCE_VALU = 2
 };
 
 /*
@@ -167,8 +172,8 @@ enum pa_decode_flags {
  *                     each run is reduced on its own and the runs are merged.
  *                     A value >= max_blocks_per_seq * B gives the single-pass
  *                     kernel.
- *   flags             0 or PA_DECODE_SHARED_BLOCKS (a hint, see above);
- *                     other bits give PA_ERR_INVALID_ARG.
+ *   flags             0, PA_DECODE_SHARED_BLOCKS (a hint, see above) and/or
+ *                     PA_DECODE_FORCE_VALU; other bits give PA_ERR_INVALID_ARG.
  * The split is exact up to rounding: the streaming softmax is associative.
  *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
  *    online softmax ("FlashAttention style")]

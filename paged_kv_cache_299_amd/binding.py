@@ -9,8 +9,9 @@ Shapes (see layout.py for the pool format):
   pa_write_kv(k_new [T,Hkv,D], v_new [T,Hkv,D], k_cache, v_cache, slot_mapping int64 [T])
   pa_decode(q [S,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
-    (calls pa_decode, or pa_decode_ex when a partition length or the
-    PA_DECODE_SHARED_BLOCKS hint (shared_blocks) is given)
+    (calls pa_decode, or pa_decode_ex when a partition length, the
+    PA_DECODE_SHARED_BLOCKS hint (shared_blocks) or PA_DECODE_FORCE_VALU
+    (force_valu: the VALU kernel on 16-bit data, for measurement) is given)
   pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, group_start int32 [NG+1],
                     prefix_blocks int32 [NG], scale, out, max_group_size=None)
   pa_prefill(q [T,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
@@ -35,6 +36,7 @@ _lib = None
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(5)
 PA_DECODE_SHARED_BLOCKS = 1
+PA_DECODE_FORCE_VALU = 2
 
 # every symbol include/pa.h declares
 EXPORTS = (
@@ -206,7 +208,7 @@ def pa_write_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               out: torch.Tensor, stream=None, partition_tokens: Optional[int] = 0,
-              shared_blocks: bool = False) -> None:
+              shared_blocks: bool = False, force_valu: bool = False) -> None:
     NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
     _need(out.shape == q.shape and out.dtype == q.dtype == k_cache.dtype,
@@ -219,7 +221,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     for t in (q, out, block_tables, context_lens):
         _need(t.is_contiguous() and t.device == k_cache.device, "inputs must be contiguous, same GPU")
     lib = load_library()
-    if not partition_tokens and not shared_blocks:  # the plain entry point
+    if not partition_tokens and not shared_blocks and not force_valu:  # the plain entry point
         rc = lib.pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D, B,
                            block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
@@ -229,7 +231,8 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D, B,
                               block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
                               int(partition_tokens or 0),
-                              PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+                              (PA_DECODE_SHARED_BLOCKS if shared_blocks else 0)
+                              | (PA_DECODE_FORCE_VALU if force_valu else 0),
                               _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
 

@@ -421,8 +421,12 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads %d is not a multiple of %d",
                     num_heads, num_kv_heads);
     if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale is not finite");
-    if (flags & ~PA_DECODE_SHARED_BLOCKS)
+    if (flags & ~(PA_DECODE_SHARED_BLOCKS | PA_DECODE_FORCE_VALU))
         return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown flags 0x%x", flags);
+    const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
+    if (force_valu && (block_size != kBlock || k_new || v_new))
+        return fail(PA_ERR_UNSUPPORTED, "pa_decode: PA_DECODE_FORCE_VALU takes block_size 16 "
+                    "and no appended token");
     if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % kBlock != 0 ||
                                                           partition_tokens > kMaxPartition)))
         return fail(PA_ERR_INVALID_ARG,
@@ -465,7 +469,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
 
     const int G = num_heads / num_kv_heads;
     const int max_tokens = max_blocks_per_seq * block_size;
-    const bool mfma = dtype != PA_F32 && G <= 16;
+    const bool mfma = dtype != PA_F32 && G <= 16 && !force_valu;
 
     int P = partition_tokens > 0
                 ? partition_tokens

@@ -166,14 +166,28 @@ def tiny(seed: int = 1, fill: bool = True) -> DecodeCase:
 
 
 def llama3_8b(seed: int = 2, num_seqs: int = 32, fill: bool = True,
-              block_size: int = 16) -> DecodeCase:
-    """Block sizes other than 16 keep the pool's token capacity (12,000 x 16)."""
+              block_size: int = 16, max_tokens: int = 4096) -> DecodeCase:
+    """Block sizes other than 16 keep the pool's token capacity (12,000 x 16);
+    max_tokens is the block tables' capacity (the lengths stay U{128..4096})."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(128, 4096, size=num_seqs, endpoint=True)
     return make_decode_case("llama3_8b", seed=seed, context_lens=ctx, num_heads=32,
                             num_kv_heads=8, head_dim=128, block_size=block_size,
-                            num_blocks=12000 * 16 // block_size, max_blocks=4096 // block_size,
-                            dtype=torch.bfloat16, rng=rng, fill=fill)
+                            num_blocks=12000 * 16 // block_size,
+                            max_blocks=max_tokens // block_size, dtype=torch.bfloat16, rng=rng,
+                            fill=fill)
+
+
+def many_seqs(seed: int = 6, num_seqs: int = 512, fill: bool = True) -> DecodeCase:
+    """512 sequences of U{128..600} tokens, Llama-3-8B heads (32 q / 8 kv, D 128,
+    bf16), tables of 40 blocks: the unit search walks 8 rounds of 64 sequences."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(128, 600, size=num_seqs, endpoint=True)
+    need = int(sum(-(-int(c) // 16) for c in ctx))
+    return make_decode_case("many_seqs", seed=seed, context_lens=ctx, num_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16,
+                            num_blocks=need + 512, max_blocks=40, dtype=torch.bfloat16, rng=rng,
+                            fill=fill)
 
 
 def opt_13b(seed: int = 3, num_seqs: int = 64, fill: bool = True) -> DecodeCase:
@@ -443,6 +457,8 @@ def shared_prefix_groups(block_tables: torch.Tensor, context_lens: torch.Tensor,
 CASES = {
     "tiny": tiny,
     "llama3_8b": llama3_8b,
+    "llama3_8b_table128k": lambda **kw: llama3_8b(max_tokens=131072, **kw),
+    "many_seqs": many_seqs,
     "opt_13b": opt_13b,
     "parallel_sampling": lambda **kw: parallel_sampling(cow=False, **kw),
     "parallel_sampling_cow": lambda **kw: parallel_sampling(cow=True, **kw),

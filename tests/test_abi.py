@@ -74,7 +74,8 @@ def _decode(lib, **kw):
     (dict(scale=float("inf")), INVALID),
     (dict(P=20), INVALID),
     (dict(P=2048), INVALID),
-    (dict(flags=2), INVALID),
+    (dict(flags=4), INVALID),
+    (dict(flags=2, B=32), UNSUPPORTED),          # the VALU kernel takes 16-token blocks
     (dict(B=24), UNSUPPORTED),
     (dict(B=32, dtype=F32), UNSUPPORTED),        # block sizes 8 / 32: matrix-core kernel only
     (dict(B=32, Hq=136, Hkv=4), UNSUPPORTED),    # more than 16 query heads per kv head

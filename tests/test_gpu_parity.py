@@ -205,14 +205,20 @@ def test_copy_blocks_bit_exact(dev):
 # times (automatic partitioning)
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["llama3_8b", "opt_13b", "parallel_sampling",
-                                  "parallel_sampling_cow", "long_ctx"])
+                                  "parallel_sampling_cow", "long_ctx",
+                                  # launches sized by the table capacity (8,192 entries) and
+                                  # a unit search over 8 rounds of 64 sequences
+                                  "llama3_8b_table128k", "many_seqs"])
 def test_workload_full_size(dev, name):
     log(f"workload {name}: generating")
     case = workloads.CASES[name]()
     P = case.partition_tokens or 0
-    run_full_case(case, dev, partition_tokens=P, strict=True)
+    # 16,384 rows of the 512-sequence case include outputs of magnitude >= 1,
+    # where bf16's own rounding exceeds 2e-3: the bound beyond that floor
+    strict = name != "many_seqs"
+    run_full_case(case, dev, partition_tokens=P, strict=strict)
     if P:
-        run_full_case(case, dev, partition_tokens=0, strict=True)
+        run_full_case(case, dev, partition_tokens=0, strict=strict)
 
 
 @pytest.mark.parametrize("name", ["llama3_8b", "edge"])
@@ -452,3 +458,37 @@ def test_decode_append_skips_out_of_range_entry(dev):
                         dtype=CODE[case.dtype])
     keep = [s for s in range(case.num_seqs) if s != bad_seq]
     check_decode(out.cpu()[keep], ref[keep], case.dtype, "append, one bad entry")
+
+
+# --------------------------------------------------------------------------
+# PA_DECODE_FORCE_VALU: the one-head VALU kernel on 16-bit data (the matrix-
+# core kernel's alternative, kept measurable), against the oracle
+# --------------------------------------------------------------------------
+def _force_valu_run(case, dev, P):
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    out = torch.full_like(g.q, float("nan"))
+    pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, out, partition_tokens=P,
+                 force_valu=True)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (32, 8), (8, 1)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_force_valu_on_16_bit_data(dev, dtype, Hq, Hkv, D):
+    case = _case(EDGE_CTX, Hq, Hkv, D, dtype, seed=Hq * 7 + Hkv + D)
+    kc, vc = oracle_apply_steps(case)
+    ref = oracle_decode(case, kc, vc)
+    for P in (0, 16, 256):
+        check_decode(_force_valu_run(case, dev, P), ref, dtype,
+                     f"force_valu {dtype} Hq={Hq} Hkv={Hkv} D={D} P={P}")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "opt_13b"])
+def test_force_valu_full_size(dev, name):
+    case = workloads.CASES[name]()
+    kc, vc = oracle_apply_steps(case)
+    check_decode(_force_valu_run(case, dev, 0), oracle_decode(case, kc, vc), case.dtype,
+                 f"force_valu {name}", strict=True)
