@@ -36,6 +36,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 WARM_S = 0.1  # untimed GPU work before each timed phase (see warm_graph())
 
 WORKLOAD_TEXT = {
+    "tiny": "tiny paged decode: 1 sequence, 1 head, D 64, B 16, context 100 -> write token "
+            "100 -> 101, 16 physical blocks in random order, fp32 (latency)",
     "llama3_8b": "Llama-3-8B-shaped GQA decode, one layer: 32 seqs, 32 q / 8 kv heads, D 128, "
                  "B 16, ctx ~ U{128..4096}, pool 12,000 blocks, bf16",
     "llama3_8b_table128k": "the Llama-3-8B-shaped batch with block tables of 131,072-token "
