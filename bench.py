@@ -338,10 +338,13 @@ def main():
             pa.pa_decode(q, k, v, bt, cl, case.scale, out, partition_tokens=part,
                          shared_blocks=shared, force_valu=args.force_valu)
 
-    # eager warmup on the capture stream (grows the library's workspace for it)
+    # eager warmup on the capture stream (grows the library's workspace for it;
+    # the plain pa_decode phase below may need a larger one than `part`)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             enqueue(i % L)
+        if part and not args.cascade and not append and not args.force_valu:
+            enqueue(0, plain=True)
     torch.cuda.synchronize()
 
     # HIP graphs: launching a decode step from Python (ctypes marshalling of

@@ -178,7 +178,10 @@ constexpr int kMaxPartitions = 1 << 16;
 //  * rows >= 2048 (e.g. 64 sequences x 40 heads): the rows alone fill the
 //    machine, and short units (P = 256) keep it evenly loaded to the end
 //    (more units than resident waves, so finished ones are replaced):
-//    OPT-13B-shaped MHA 156 us at P = 256 vs 162 us at P = 1024;
+//    OPT-13B-shaped MHA 156 us at P = 256 vs 162 us at P = 1024 -- unless
+//    the tables hold at most 1024 tokens: then one pass per row needs no
+//    merge (512 sequences of U{128..600} tokens, tables of 640: 132.4 us in
+//    one pass against 148.0 at P = 256 and 139.5 at P = 512);
 //  * fewer rows (32 sequences x 8 kv heads): rows must be split for
 //    parallelism, and long units cut the partials the merge reads: the
 //    longest P <= 1024 with >= 1024 units (Llama-3-8B-shaped: P = 1024,
@@ -186,7 +189,7 @@ constexpr int kMaxPartitions = 1 << 16;
 //  * the VALU kernel (fp32 data or more than 16 query heads per kv head)
 //    does more arithmetic per byte and takes P <= 512 with >= 2048 units.
 int auto_partition(bool mfma, int64_t rows, int max_tokens) {
-    if (mfma && rows >= 2048) return 256;
+    if (mfma && rows >= 2048) return max_tokens <= kMaxPartition ? kMaxPartition : 256;
     const int longest = mfma ? 1024 : 512;
     const int64_t min_units = mfma ? 1024 : 2048;
     for (int P = longest; P > 256; P /= 2)
