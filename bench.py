@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=None,
                     help="partition tokens for pa_decode (default: the workload's, else auto)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions (0 = skip)")
+    ap.add_argument("--cpu-single-reps", type=int, default=1,
+                    help="decode: oracle repetitions on one thread, after the all-core ones")
     ap.add_argument("--seed", type=int, default=None,
                     help="draw of the workload (default: the workload's own seed)")
     ap.add_argument("--cascade", action="store_true",
@@ -444,19 +446,32 @@ def main():
         torch.cuda.synchronize()
         kh, vh = raw_bits(k0.cpu()), raw_bits(v0.cpu())
         code = pa.DTYPE_CODES[dt]
-        times = []
-        for _ in range(args.cpu_reps):
-            t = time.perf_counter()
-            oracle.decode(raw_bits(case.q), kh, vh, case.block_tables.numpy(),
-                          case.context_lens.numpy(), case.scale, num_kv_heads=Hkv, head_dim=D,
-                          block_size=B, k_x=16 // e, dtype=code)
-            times.append(time.perf_counter() - t)
-        t_med = statistics.median(times)
+
+        def oracle_seconds(reps):
+            times = []
+            for _ in range(reps):
+                t = time.perf_counter()
+                oracle.decode(raw_bits(case.q), kh, vh, case.block_tables.numpy(),
+                              case.context_lens.numpy(), case.scale, num_kv_heads=Hkv,
+                              head_dim=D, block_size=B, k_x=16 // e, dtype=code)
+                times.append(time.perf_counter() - t)
+            return statistics.median(times)
+
+        t_med = oracle_seconds(args.cpu_reps)
         cpu = {"value": round(dec_bytes / t_med / 1e9, 3), "unit": "GB/s",
                "tokens_per_s": round(S / t_med, 2), "seconds": round(t_med, 3),
                "cores": oracle.num_threads(), "kind": "oracle", **host_info(),
                "sample": f"the full workload (all {S} sequences, layer 0), pa_decode only, "
                          f"median of {args.cpu_reps} runs, fp64"}
+        if args.cpu_single_reps > 0:
+            prev = oracle.set_num_threads(1)
+            try:
+                t1 = oracle_seconds(args.cpu_single_reps)
+            finally:
+                oracle.set_num_threads(prev)
+            cpu["single_core"] = {"value": round(dec_bytes / t1 / 1e9, 3), "unit": "GB/s",
+                                  "tokens_per_s": round(S / t1, 2), "seconds": round(t1, 3),
+                                  "cores": 1, "runs": args.cpu_single_reps}
         del kh, vh
 
     rec = {

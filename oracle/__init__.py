@@ -8,5 +8,5 @@ from .oracle import (  # noqa: F401
     decode, decode_partitioned, prefill, write_kv, copy_blocks, swap_blocks,
     kv_cache_bytes, blocks_for_tokens, slot_of,
     f16_bits_to_float64, bf16_bits_to_float64,
-    OracleError, num_threads,
+    OracleError, num_threads, set_num_threads,
 )

@@ -20,7 +20,8 @@ F32, F16, BF16 = 0, 1, 2
 _ELEM = {F32: 4, F16: 2, BF16: 2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of the same source (the sanitizer run uses it)
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _ERRORS = {
@@ -74,6 +75,8 @@ def _load():
     lib.oracle_bf16_to_double.restype = D
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I32
+    lib.oracle_set_num_threads.argtypes = [I32]
+    lib.oracle_set_num_threads.restype = I32
     _lib = lib
     return lib
 
@@ -97,6 +100,13 @@ def _raw(a, dtype):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Thread count for later oracle calls from this thread; returns the previous one."""
+    if n < 1:
+        raise OracleError("thread count must be >= 1")
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, *, num_kv_heads, head_dim,

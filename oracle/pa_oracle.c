@@ -468,3 +468,12 @@ int64_t oracle_slot_of(const int32_t *block_table_row, int64_t B, int64_t i) {
 
 /* Threads the OpenMP loops above will use (for reporting the CPU baseline). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Sets the thread count of the calling thread's later OpenMP loops (n >= 1);
+ * returns the previous count.  Each output is computed by one thread, so the
+ * results do not depend on it. */
+int oracle_set_num_threads(int n) {
+    int prev = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return prev;
+}

@@ -31,7 +31,8 @@ import torch
 from .layout import DTYPE_CODES, k_chunk
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY names another build of the same sources (the host-sanitizer run uses it)
+_LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 _lib = None
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(5)

@@ -33,8 +33,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every source into one shared library at `out` (always recompiles)."""
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, *extra_flags, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -45,8 +46,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

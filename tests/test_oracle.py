@@ -160,6 +160,21 @@ def test_decode_equals_dense_softmax_attention(dtype, Hq, Hkv):
         np.testing.assert_allclose(out[s], ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def test_decode_does_not_depend_on_the_thread_count():
+    """The single-core baseline times the same computation: one thread per output."""
+    rng = np.random.default_rng(31)
+    q, kp, vp, tables, ctx, _, x = _paged_case(rng, [1, 40, 300, 77, 16], 8, 2, 32, 16, BF16)
+    many = _oracle_decode(q, kp, vp, tables, ctx, 0.17, 2, 32, 16, BF16, x)
+    prev = oracle.set_num_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        one = _oracle_decode(q, kp, vp, tables, ctx, 0.17, 2, 32, 16, BF16, x)
+    finally:
+        oracle.set_num_threads(prev)
+    assert oracle.num_threads() == prev
+    assert np.array_equal(many, one)
+
+
 def test_decode_brute_force_tiny_shapes():
     """Every tiny geometry: block sizes 1/2/4, dims 1..3, ctx 0..9, three head groupings."""
     rng = np.random.default_rng(7)
