@@ -10,13 +10,16 @@ independent KV pools (one per model layer, all sharing the block tables, as
 a real decode iteration does), so no step finds its K/V in the caches of the
 previous one.
 
-Steps are launched as HIP graph replays, one captured graph per pass over the
-layers: an eager launch from Python costs about as much host time as the GPU
-work, and every graph launch adds a few microseconds of GPU idle time.
+Decode steps are launched as HIP graph replays, one captured graph per decode
+iteration of a 32-layer model (`--graph-steps`; layer i of the iteration reads
+pool i % `--layers`): an eager launch from Python costs about as much host time
+as the GPU work, and every graph launch adds a few microseconds of GPU idle
+time, once per iteration as in a serving loop.
 
 Prints ONE JSON line.  `value` = algorithmic bytes of the step / step time
 (GB/s, decimal), tokens/s = sequences / step time.  `roofline` covers
-pa_decode (its partition kernel plus the merge kernel), timed with HIP events
+pa_decode (its partition kernel, and the merge kernel where the merge is not
+inside it), timed with HIP events
 on the launch stream over graph replays of the decode alone.  `cpu_baseline` times the CPU oracle on the same
 inputs (layer 0) on this host's cores.
 """
@@ -77,6 +80,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--layers", type=int, default=8, help="resident KV pools rotated per step")
+    ap.add_argument("--graph-steps", type=int, default=32,
+                    help="decode workloads: steps per captured graph, one decode iteration "
+                         "of a 32-layer model (layer i on pool i %% --layers)")
     ap.add_argument("--partition", type=int, default=None,
                     help="partition tokens for pa_decode (default: the workload's, else auto)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions (0 = skip)")
@@ -351,25 +357,30 @@ def main():
 
     # HIP graphs: launching a decode step from Python (ctypes marshalling of
     # two calls) takes about as long as the GPU work, and each graph launch
-    # leaves the GPU idle for several microseconds, so one graph holds a whole
-    # pass over the layers -- as a model's decode iteration would be captured.
-    # Replays are idempotent: the writes store the same tokens in the same slots.
-    def capture(layers, **phase):
+    # leaves the GPU idle for several microseconds, so one graph holds the
+    # steps of one decode iteration of the model (--graph-steps, 32 layers as
+    # in Llama-3-8B), layer i of the iteration on pool i % L -- as a serving
+    # loop captures its decode iteration.  Replays are idempotent: the writes
+    # store the same tokens in the same slots.
+    G = max(1, args.graph_steps)
+
+    def capture(steps, **phase):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for l in layers:
-                enqueue(l, **phase)
+            for i in range(steps):
+                enqueue(i % L, **phase)
         return g
 
     def timed(n, **phase):
-        """Runs exactly n steps of the phase (layer i % L for step i) as graph
-        replays; wall seconds and GPU ms (HIP events on the launch stream)."""
-        q_, r_ = divmod(n, L)
-        g_all = capture(range(L), **phase)
-        g_rest = capture(range(r_), **phase) if r_ else None
+        """Runs exactly n steps of the phase as graph replays (G steps per
+        graph, a shorter graph for the rest); wall seconds and GPU ms (HIP
+        events on the launch stream)."""
+        q_, r_ = divmod(n, G)
+        g_all = capture(G, **phase) if q_ else None
+        g_rest = capture(r_, **phase) if r_ else None
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        warm_graph(g_all, stream)
+        warm_graph(g_all if g_all is not None else g_rest, stream)
         with torch.cuda.stream(stream):
             if g_rest is not None:
                 g_rest.replay()
@@ -387,8 +398,8 @@ def main():
 
     def spread(passes=25, **phase):
         """p10 / median / p90 of the per-step GPU time over graph replays of
-        one pass over the layers each (events between replays)."""
-        g_all = capture(range(L), **phase)
+        G steps each (events between replays)."""
+        g_all = capture(G, **phase)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
         warm_graph(g_all, stream)
         with torch.cuda.stream(stream):
@@ -397,9 +408,9 @@ def main():
                 g_all.replay()
                 ev[i + 1].record(stream)
             torch.cuda.synchronize()
-        per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / L for i in range(passes))
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / G for i in range(passes))
         return {"p10": round(per[len(per) // 10], 2), "median": round(per[len(per) // 2], 2),
-                "p90": round(per[(9 * len(per)) // 10], 2), "passes": passes, "steps_each": L}
+                "p90": round(per[(9 * len(per)) // 10], 2), "passes": passes, "steps_each": G}
 
     # timed region: exactly `steps` steps
     wall, step_gpu_ms = timed(args.steps)
@@ -498,7 +509,7 @@ def main():
                    "append": bool(append),
                    "kernel": "valu (PA_DECODE_FORCE_VALU)" if args.force_valu else None,
                    "groups": int(pb.shape[0]), "max_group_size": int(max_group),
-                   "layers_rotated": args.layers},
+                   "layers_rotated": args.layers, "steps_per_graph": G},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "step_bytes": int(step_bytes),
@@ -509,17 +520,25 @@ def main():
                          else "pa_decode_append" if append
                          else f"pa_decode_ex (partition_tokens {part})" if part or shared
                          else "pa_decode"),
+        "merge": (None if args.cascade else
+                  {0: "none (one partition per table)", 1: "merge kernel",
+                   2: "in the partition kernel"}[
+                      pa.pa_decode_merge_mode(S, Hq, Hkv, D, B, case.max_blocks, dt, part,
+                                              shared_blocks=shared,
+                                              force_valu=args.force_valu)]),
         "logical_bytes": int(dec_bytes),
         "unique_bytes": int(uniq_bytes),
         "write_us": round(wr_avg * 1e3, 2) if wr_avg is not None else None,
-        "launch": "HIP graph replays, one graph per pass over the rotated layers",
+        "launch": f"HIP graph replays, {G} steps per graph (one decode iteration of a "
+                  f"{G}-layer model), layer pools rotated",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
                      "kernel": ("pa_decode_cascade (unit + merge kernels)" if args.cascade
                                 else "pa_decode_append (partition kernel storing the new "
                                      "tokens + merge kernel)" if append
-                                else "pa_decode (partition + merge kernels)"),
+                                else "pa_decode (partition kernel, and the merge kernel "
+                                     "where the merge is not in the partition kernel)"),
                      "bytes_per_launch": int(roof_bytes)},
         "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
         "decode_plain": None if plain_us is None else {
@@ -858,7 +877,8 @@ def bench_vattention(args, dev):
         "step_map_ms": round(step_ms, 2),
         "create_us_per_page": round(info["create_us_per_page"], 2),
         "map_us_per_page": round(info["map_us_per_page"], 2),
-        "launch": "HIP graph replays, one graph per pass over the rotated layers",
+        "launch": f"HIP graph replays, {G} steps per graph (one decode iteration of a "
+                  f"{G}-layer model), layer pools rotated",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "kernel": "pa_vkv_decode (partition + merge kernels, no block table)",

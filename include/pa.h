@@ -159,7 +159,11 @@ enum pa_decode_flags {
      * products and P.V on the vector ALUs) on 16-bit data too, where the
      * matrix-core kernel would run; same results within the tolerance.
      * block_size 16 only (PA_ERR_UNSUPPORTED otherwise). */
-    PA_DECODE_FORCE_VALU = 2
+    PA_DECODE_FORCE_VALU = 2,
+    /* Merge split contexts with the separate merge kernel even where the
+     * partition kernel would merge them itself (pa_decode_merge_mode); same
+     * bits either way. */
+    PA_DECODE_MERGE_KERNEL = 4
 };
 
 /*
@@ -172,8 +176,9 @@ enum pa_decode_flags {
  *                     each run is reduced on its own and the runs are merged.
  *                     A value >= max_blocks_per_seq * B gives the single-pass
  *                     kernel.
- *   flags             0, PA_DECODE_SHARED_BLOCKS (a hint, see above) and/or
- *                     PA_DECODE_FORCE_VALU; other bits give PA_ERR_INVALID_ARG.
+ *   flags             0, or PA_DECODE_SHARED_BLOCKS (a hint, see above),
+ *                     PA_DECODE_FORCE_VALU, PA_DECODE_MERGE_KERNEL or'd;
+ *                     other bits give PA_ERR_INVALID_ARG.
  * The split is exact up to rounding: the streaming softmax is associative.
  *   [論文解説: PagedAttention, 技術的詳細 › PagedAttentionアルゴリズム,
  *    online softmax ("FlashAttention style")]
@@ -190,12 +195,13 @@ int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
  * harnesses that forbid allocation.  Same arguments, same kernels, and the
  * same bits as pa_decode_ex with the same partition length; the partials of
  * split contexts go to a static device array of 32 MiB in the library (one
- * per GPU, held until the process ends) instead of the per-stream workspace.
+ * per GPU, held until the process ends) instead of the per-stream workspace,
+ * and so do the in-kernel merge's row counters.
  *   Limit: num_seqs * num_heads * ceil(max_blocks_per_seq * B / P) *
- *   (head_dim + 2) * 4 bytes of partials at most 32 MiB - 256
- *   (PA_ERR_UNSUPPORTED beyond, before anything is enqueued; e.g. 32
- *   sequences x 32 heads of up to 131,072 tokens at P = 1024, or 128 of up to
- *   4,096 at P = 256).
+ *   (head_dim + 2) * 4 bytes of partials at most 32 MiB - 16,640
+ *   (PA_ERR_UNSUPPORTED beyond, before anything is enqueued; at head_dim 128,
+ *   e.g. 32 sequences x 32 heads with tables of up to 63,488 tokens at
+ *   P = 1024, or 128 x 32 of up to 3,840 tokens at P = 256).
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents: calls that overlap in time on one GPU (on different streams, or
  * graph replays running concurrently) race and give wrong results.  Nothing
@@ -460,6 +466,36 @@ const char *pa_last_error(void);
  */
 int pa_decode_plan(const int32_t *context_lens, int num_seqs, int num_heads, int num_kv_heads,
                    int block_size, int max_blocks_per_seq, int dtype, int *partition_tokens);
+
+/*
+ * pa_decode_merge_mode -- how pa_decode_ex merges split contexts for these
+ * sizes, partition length and flags on the current device, for a stream that
+ * is not being captured:
+ *   PA_MERGE_NONE (0)       one partition covers every table: nothing to merge;
+ *   PA_MERGE_KERNEL (1)     a merge kernel follows the partition kernel;
+ *   PA_MERGE_IN_KERNEL (2)  the unit of each split (sequence, kv head) that
+ *                           finishes last merges it inside the partition
+ *                           kernel, through the L2 of the one XCD that ran all
+ *                           of that row's units.  Taken for the matrix-core
+ *                           kernel at block size 8 or 16 when num_kv_heads is
+ *                           a multiple of 8, rows have at most 8 partitions
+ *                           and 512 outputs (G * head_dim), the launch has at
+ *                           most 2,048 work units (num_seqs * num_kv_heads *
+ *                           partitions), PA_DECODE_MERGE_KERNEL is not set,
+ *                           and the device's dispatcher places workgroups b
+ *                           and b + 8 of a launch on one XCD (checked once per
+ *                           device by a small probe launch, which this call
+ *                           or the first decode makes and waits for).  A
+ *                           stream under capture, or one whose counter buffer
+ *                           would have to grow during capture, takes the merge
+ *                           kernel instead.
+ * Same bits in every mode: the partitions are folded in the same order.
+ * A negative value is -(status) for bad arguments (PA_ERR_INVALID_ARG).
+ */
+enum pa_merge_mode { PA_MERGE_NONE = 0, PA_MERGE_KERNEL = 1, PA_MERGE_IN_KERNEL = 2 };
+int pa_decode_merge_mode(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int dtype,
+                         int partition_tokens, int flags);
 
 /* Bytes of workspace pa_decode_ex would use for these sizes (0 = none). */
 int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,

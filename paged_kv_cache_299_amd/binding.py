@@ -11,7 +11,8 @@ Shapes (see layout.py for the pool format):
             scale, out [S,Hq,D], stream=None, partition_tokens=0, shared_blocks=False)
     (calls pa_decode, or pa_decode_ex when a partition length, the
     PA_DECODE_SHARED_BLOCKS hint (shared_blocks) or PA_DECODE_FORCE_VALU
-    (force_valu: the VALU kernel on 16-bit data, for measurement) is given)
+    (force_valu: the VALU kernel on 16-bit data, for measurement) or
+    PA_DECODE_MERGE_KERNEL (merge_kernel: the separate merge kernel) is given)
   pa_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, group_start int32 [NG+1],
                     prefix_blocks int32 [NG], scale, out, max_group_size=None)
   pa_prefill(q [T,Hq,D], k_cache, v_cache, block_tables int32 [S,MB], context_lens int32 [S],
@@ -38,6 +39,8 @@ _lib = None
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_MEMORY = range(5)
 PA_DECODE_SHARED_BLOCKS = 1
 PA_DECODE_FORCE_VALU = 2
+PA_DECODE_MERGE_KERNEL = 4
+PA_MERGE_NONE, PA_MERGE_KERNEL, PA_MERGE_IN_KERNEL = 0, 1, 2
 
 # every symbol include/pa.h declares
 EXPORTS = (
@@ -49,7 +52,8 @@ EXPORTS = (
     "pa_vkv_create", "pa_vkv_info", "pa_vkv_layer", "pa_vkv_alloc_reqid", "pa_vkv_step",
     "pa_vkv_free_reqid", "pa_vkv_reclaim", "pa_vkv_destroy", "pa_vkv_write_kv", "pa_vkv_decode",
     "pa_status_str",
-    "pa_last_error", "pa_decode_plan", "pa_decode_workspace_bytes", "pa_release_workspaces",
+    "pa_last_error", "pa_decode_plan", "pa_decode_merge_mode", "pa_decode_workspace_bytes",
+    "pa_release_workspaces",
     "pa_version", "pa_set_debug",
 )
 
@@ -121,6 +125,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_decode_plan.argtypes = [P, I32, I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
     lib.pa_decode_plan.restype = I32
+    lib.pa_decode_merge_mode.argtypes = [I32] * 9
+    lib.pa_decode_merge_mode.restype = I32
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = I64
     lib.pa_release_workspaces.argtypes = []
@@ -209,7 +215,8 @@ def pa_write_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
 def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               out: torch.Tensor, stream=None, partition_tokens: Optional[int] = 0,
-              shared_blocks: bool = False, force_valu: bool = False) -> None:
+              shared_blocks: bool = False, force_valu: bool = False,
+              merge_kernel: bool = False) -> None:
     NB, Hkv, D, B = _cache_dims(k_cache, v_cache)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
     _need(out.shape == q.shape and out.dtype == q.dtype == k_cache.dtype,
@@ -222,7 +229,7 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     for t in (q, out, block_tables, context_lens):
         _need(t.is_contiguous() and t.device == k_cache.device, "inputs must be contiguous, same GPU")
     lib = load_library()
-    if not partition_tokens and not shared_blocks and not force_valu:  # the plain entry point
+    if not (partition_tokens or shared_blocks or force_valu or merge_kernel):  # the plain entry
         rc = lib.pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), S, Hq, Hkv, D, B,
                            block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
@@ -233,7 +240,8 @@ def pa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               block_tables.shape[1], NB, DTYPE_CODES[q.dtype],
                               int(partition_tokens or 0),
                               (PA_DECODE_SHARED_BLOCKS if shared_blocks else 0)
-                              | (PA_DECODE_FORCE_VALU if force_valu else 0),
+                              | (PA_DECODE_FORCE_VALU if force_valu else 0)
+                              | (PA_DECODE_MERGE_KERNEL if merge_kernel else 0),
                               _stream_handle(stream, q.device))
     _check(rc, "pa_decode")
 
@@ -276,6 +284,24 @@ def pa_decode_plan(context_lens, num_heads: int, num_kv_heads: int, block_size: 
                                        ctypes.byref(out))
     _check(rc, "pa_decode_plan")
     return int(out.value)
+
+
+def pa_decode_merge_mode(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                         block_size: int, max_blocks_per_seq: int, dtype: torch.dtype,
+                         partition_tokens: int = 0, shared_blocks: bool = False,
+                         force_valu: bool = False, merge_kernel: bool = False) -> int:
+    """How pa_decode merges split contexts for these sizes on the current device:
+    PA_MERGE_NONE, PA_MERGE_KERNEL or PA_MERGE_IN_KERNEL."""
+    flags = ((PA_DECODE_SHARED_BLOCKS if shared_blocks else 0)
+             | (PA_DECODE_FORCE_VALU if force_valu else 0)
+             | (PA_DECODE_MERGE_KERNEL if merge_kernel else 0))
+    r = load_library().pa_decode_merge_mode(int(num_seqs), int(num_heads), int(num_kv_heads),
+                                            int(head_dim), int(block_size),
+                                            int(max_blocks_per_seq), DTYPE_CODES[dtype],
+                                            int(partition_tokens or 0), flags)
+    if r < 0:
+        _check(-r, "pa_decode_merge_mode")
+    return int(r)
 
 
 def pa_read_tiles(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,

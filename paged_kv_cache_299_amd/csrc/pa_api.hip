@@ -13,6 +13,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -71,16 +72,29 @@ struct Workspace {
     std::vector<void *> retired;
 };
 std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// kind kPartials: the split partials (any contents between calls).  kind
+// kTickets: the in-kernel merge's row counters, zeroed when allocated and left
+// at zero by every call -- a buffer of its own, so that no partial of a later
+// call with other sizes ever lands on a counter.
+enum WorkspaceKind { kPartials = 0, kTickets = 1 };
+std::map<std::tuple<int, hipStream_t, int>, Workspace> g_ws;
 
-int workspace_for(hipStream_t stream, size_t need, void **out) {
+// The stream's buffer of `kind`, grown to `need` bytes.  may_grow false (the
+// stream is being captured): *out is null when the buffer is too small.
+int workspace_for(hipStream_t stream, size_t need, void **out, int kind = kPartials,
+                  bool may_grow = true) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[{dev, stream}];
+    Workspace &w = g_ws[{dev, stream, kind}];
     if (w.bytes < need) {
-        size_t bytes = need < (size_t)(1 << 20) ? (size_t)(1 << 20) : need;
+        if (!may_grow) {
+            *out = nullptr;
+            return PA_OK;
+        }
+        const size_t least = kind == kTickets ? (size_t)(64 << 10) : (size_t)(1 << 20);
+        size_t bytes = need < least ? least : need;
         if (bytes < 2 * w.bytes) bytes = 2 * w.bytes;  // geometric growth
         void *p = nullptr;
         e = hipMalloc(&p, bytes);
@@ -88,6 +102,13 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
             (void)hipGetLastError();
             return fail(PA_ERR_NO_MEMORY, "workspace of %zu bytes: %s", bytes,
                         hipGetErrorString(e));
+        }
+        if (kind == kTickets) {
+            e = hipMemset(p, 0, bytes);  // synchronous: done before anything is queued
+            if (e != hipSuccess) {
+                (void)hipFree(p);
+                return hip_fail(e, "workspace hipMemset");
+            }
         }
         if (w.ptr) w.retired.push_back(w.ptr);
         w.ptr = p;
@@ -105,8 +126,16 @@ int workspace_for(hipStream_t stream, size_t need, void **out) {
 // in time on one GPU.  In host code `scratch` is a stand-in, not a device
 // address: its device address comes from hipGetSymbolAddress, once per
 // device, and only that address is used.
+// Layout: [0, 256) the PA_DEBUG flags word; then the in-kernel merge's row
+// counters (zero between calls: the array starts at zero and every call
+// leaves them so) and PA_DEBUG's per-row XCD bits, 2,048 rows each; then the
+// partials.
 constexpr size_t kScratchBytes = (size_t)32 << 20;  // 32 MiB
-constexpr size_t kScratchFlags = 256;                // PA_DEBUG flags word, then partials
+constexpr size_t kScratchRows = 2048;
+constexpr size_t kScratchTickets = 256;
+constexpr size_t kScratchSeen = kScratchTickets + kScratchRows * sizeof(int);
+constexpr size_t kScratchPartials = kScratchSeen + kScratchRows * sizeof(unsigned);  // 16,640
+static_assert(kScratchPartials % 256 == 0, "partials stay 256-byte aligned");
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -135,6 +164,46 @@ int scratch_address(void **out) {
     *out = g_scratch_ptr[dev];
     return PA_OK;
 }
+
+// ---- in-kernel merge: the dispatcher rule it relies on, probed per device ----
+std::mutex g_xcd_mutex;
+int g_xcd_state[kMaxDevices] = {};  // 0 not probed, 1 the rule holds, 2 it does not
+
+// Whether workgroups congruent mod 8 run on one XCD on the current device
+// (pa::probe_xcd_dispatch, once per device: X XCDs dealt in turn, X dividing
+// 8).  A stream under capture does not probe: its calls use the merge kernel
+// until a call outside capture has probed.
+bool xcd_rule_holds(bool capturing) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return false;
+    }
+    std::lock_guard<std::mutex> lock(g_xcd_mutex);
+    if (g_xcd_state[dev] == 0) {
+        if (capturing) return false;
+        int X = 0;
+        bool ok = false;
+        if (pa::probe_xcd_dispatch(&X, &ok) != hipSuccess) {
+            (void)hipGetLastError();
+            ok = false;
+        }
+        g_xcd_state[dev] = ok && X >= 1 && 8 % X == 0 ? 1 : 2;
+    }
+    return g_xcd_state[dev] == 1;
+}
+
+// A PA_DEBUG buffer of one call: the stream is drained before it is freed.
+struct DeviceBuffer {
+    void *p = nullptr;
+    hipStream_t stream = nullptr;
+    ~DeviceBuffer() {
+        if (p) {
+            (void)hipStreamSynchronize(stream);
+            (void)hipFree(p);
+        }
+    }
+};
 
 // The address a kernel uses for p: device memory as it is, pinned host memory
 // (hipHostMalloc; torch's pin_memory) through its device mapping.  Pageable
@@ -407,6 +476,58 @@ int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int
 
 namespace pa {
 
+// The partitioning a decode call takes (arguments already validated).
+struct DecodeShape {
+    bool mfma;       // matrix-core partition kernel
+    int P;           // partition length in tokens
+    int64_t NP;      // partitions per row for full tables
+    int64_t units;   // work units for full tables (the grid)
+    bool fused;      // merge inside the partition kernel (subject to the dispatch probe)
+};
+
+DecodeShape decode_shape(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int dtype,
+                         int partition_tokens, int flags) {
+    DecodeShape sh{};
+    const int G = num_heads / num_kv_heads;
+    const int max_tokens = max_blocks_per_seq * block_size;
+    // block size 8: a unit's table slice is 64 entries = 512 tokens
+    const int max_part = block_size == 8 ? 512 : kMaxPartition;
+    sh.mfma = dtype != PA_F32 && G <= 16 && !(flags & PA_DECODE_FORCE_VALU);
+    int P = partition_tokens > 0
+                ? partition_tokens
+                : std::min(auto_partition(sh.mfma,
+                                          (int64_t)num_seqs * (sh.mfma ? num_kv_heads : num_heads),
+                                          max_tokens),
+                           // block 32: a wave has a whole 16 KiB block in flight, and
+                           // shorter units stream better (Llama-3-8B step: 53.2 us at
+                           // 512 against 54.5 at 1024 and 57.4 at 256)
+                           block_size == 32 ? 512 : max_part);
+    int64_t NP = 1;
+    if (P < max_tokens) {
+        NP = num_partitions(max_tokens, P);
+    } else {
+        // one partition covers every sequence; keep P a multiple of 16 that does
+        P = max_tokens < kBlock ? kBlock : (max_tokens + kBlock - 1) / kBlock * kBlock;
+        if (P > max_part) P = max_part, NP = num_partitions(max_tokens, P);
+    }
+    sh.P = P;
+    sh.NP = NP;
+    sh.units = NP * (int64_t)num_seqs * (sh.mfma ? num_kv_heads : num_heads);
+    // In-kernel merge (merge_row_in_l2 in pa_decode.hip): the matrix-core
+    // kernel at B = 8 or 16; kv heads a multiple of 8, so that a row's units
+    // are congruent mod 8 and share an XCD; at most kFusedMaxParts partitions
+    // and 512 outputs per row, which the last unit reads back in one round
+    // trip; and every unit resident at once (kFusedMaxUnits: 3 waves per SIMD
+    // at the kernel's ~144 VGPRs hold 3,072), since a unit that keeps its slot
+    // through the ticket round trip would otherwise hold back queued units
+    // (OPT-13B-shaped step, ~6,000 units: 1 us slower than the merge kernel).
+    sh.fused = NP > 1 && sh.mfma && block_size != 32 && num_kv_heads % 8 == 0 &&
+               NP <= kFusedMaxParts && G * head_dim <= 512 && sh.units <= kFusedMaxUnits &&
+               !(flags & PA_DECODE_MERGE_KERNEL);
+    return sh;
+}
+
 // pa_decode_ex, and the decode over virtual-memory storage (block_tables ==
 // nullptr, a Contiguous description instead).
 int decode_impl(const void *q, const void *k_cache, const void *v_cache,
@@ -424,7 +545,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads %d is not a multiple of %d",
                     num_heads, num_kv_heads);
     if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale is not finite");
-    if (flags & ~(PA_DECODE_SHARED_BLOCKS | PA_DECODE_FORCE_VALU))
+    if (flags & ~(PA_DECODE_SHARED_BLOCKS | PA_DECODE_FORCE_VALU | PA_DECODE_MERGE_KERNEL))
         return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown flags 0x%x", flags);
     const bool force_valu = (flags & PA_DECODE_FORCE_VALU) != 0;
     if (force_valu && (block_size != kBlock || k_new || v_new))
@@ -471,30 +592,15 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         return fail(PA_ERR_INVALID_ARG, "pa_decode: data pointers must be 16-byte aligned");
 
     const int G = num_heads / num_kv_heads;
-    const int max_tokens = max_blocks_per_seq * block_size;
-    const bool mfma = dtype != PA_F32 && G <= 16 && !force_valu;
-
-    int P = partition_tokens > 0
-                ? partition_tokens
-                : std::min(auto_partition(mfma,
-                                          (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads),
-                                          max_tokens),
-                           // block 32: a wave has a whole 16 KiB block in flight, and
-                           // shorter units stream better (Llama-3-8B step: 53.2 us at
-                           // 512 against 54.5 at 1024 and 57.4 at 256)
-                           block_size == 32 ? 512 : max_part);
-    int64_t NP = 1;
-    if (P < max_tokens) {
-        NP = num_partitions(max_tokens, P);
-    } else {
-        // one partition covers every sequence; keep P a multiple of 16 that does
-        P = max_tokens < kBlock ? kBlock : (max_tokens + kBlock - 1) / kBlock * kBlock;
-        if (P > max_part) P = max_part, NP = num_partitions(max_tokens, P);
-    }
+    const DecodeShape sh = decode_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                        max_blocks_per_seq, dtype, partition_tokens, flags);
+    const bool mfma = sh.mfma;
+    int P = sh.P;
+    const int64_t NP = sh.NP;
     if (NP > kMaxPartitions)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld partitions (max %d)", (long long)NP,
                     kMaxPartitions);
-    const int64_t units = NP * (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads);
+    const int64_t units = sh.units;
     if (units > (int64_t)0x7fffffff - 4096)
         return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld work units", (long long)units);
 
@@ -532,12 +638,12 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         NP > 1 ? (size_t)num_seqs * num_heads * NP * (head_dim + 2) * sizeof(float) : 0;
     void *fixed = nullptr;  // pa_decode_noalloc: the static scratch
     if (no_alloc) {
-        if (part_bytes > kScratchBytes - kScratchFlags)
+        if (part_bytes > kScratchBytes - kScratchPartials)
             return fail(PA_ERR_UNSUPPORTED,
                         "pa_decode_noalloc: %zu bytes of partials (%d sequences x %d heads x %lld "
                         "partitions) exceed the %zu-byte static workspace; use pa_decode",
                         part_bytes, num_seqs, num_heads, (long long)NP,
-                        kScratchBytes - kScratchFlags);
+                        kScratchBytes - kScratchPartials);
         const int rc = scratch_address(&fixed);
         if (rc != PA_OK) return rc;
     }
@@ -553,28 +659,93 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         if (err != hipSuccess) return hip_fail(err, "pa_read_tiles launch");
         return PA_OK;
     }
+    DeviceBuffer seen_owned;  // PA_DEBUG's per-row XCD bits (in-kernel merge)
+    const int64_t rows = (int64_t)num_seqs * num_kv_heads;
     if (NP > 1) {
         void *ws = nullptr;
         const size_t o_bytes = (size_t)num_seqs * num_heads * NP * head_dim * sizeof(float);
         if (fixed) {
-            ws = (char *)fixed + kScratchFlags;
+            ws = (char *)fixed + kScratchPartials;
         } else {
             const int rc = workspace_for((hipStream_t)stream, part_bytes, &ws);
             if (rc != PA_OK) return rc;
         }
         a.part_o = (float *)ws;
         a.part_ml = (float *)((char *)ws + o_bytes);
+        if (sh.fused) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            hipError_t ce = hipStreamIsCapturing((hipStream_t)stream, &cs);
+            if (ce != hipSuccess) return hip_fail(ce, "pa_decode: hipStreamIsCapturing");
+            const bool capturing = cs != hipStreamCaptureStatusNone;
+            void *tk = nullptr;
+            if (xcd_rule_holds(capturing)) {
+                if (fixed) {
+                    tk = (char *)fixed + kScratchTickets;  // rows <= units <= kScratchRows
+                } else {
+                    // a stream under capture does not allocate: merge kernel instead
+                    const int rc = workspace_for((hipStream_t)stream, (size_t)rows * sizeof(int),
+                                                 &tk, kTickets, !capturing);
+                    if (rc != PA_OK) return rc;
+                }
+            }
+            if (tk) {
+                a.fuse_merge = 1;
+                a.ticket = (int *)tk;
+                if (pa::debug_enabled() && !capturing) {
+                    void *seen = nullptr;
+                    if (fixed) {
+                        seen = (char *)fixed + kScratchSeen;
+                    } else {
+                        hipError_t me = hipMalloc(&seen, (size_t)rows * sizeof(unsigned));
+                        if (me != hipSuccess) {
+                            (void)hipGetLastError();
+                            return fail(PA_ERR_NO_MEMORY, "pa_decode: PA_DEBUG scratch: %s",
+                                        hipGetErrorString(me));
+                        }
+                        seen_owned.p = seen;
+                        seen_owned.stream = (hipStream_t)stream;
+                    }
+                    hipError_t me = hipMemsetAsync(seen, 0, (size_t)rows * sizeof(unsigned),
+                                                   (hipStream_t)stream);
+                    if (me != hipSuccess) return hip_fail(me, "pa_decode: PA_DEBUG memset");
+                    a.xcd_seen = (unsigned *)seen;
+                }
+            }
+        }
     }
     hipError_t err = pa::launch_decode(a, dtype, head_dim,
                                        mfma ? pa::DecodeKernel::kMfma : pa::DecodeKernel::kValu,
                                        (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(err, "pa_decode launch");
+    if (a.xcd_seen)
+        return pa::debug_check_xcd(k_new ? "pa_decode_append" : "pa_decode", a.xcd_seen, rows,
+                                   (hipStream_t)stream, (unsigned *)fixed);
     return PA_OK;
 }
 
 }  // namespace pa
 
 extern "C" {
+
+int pa_decode_merge_mode(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int dtype,
+                         int partition_tokens, int flags) {
+    if (elem_bytes(dtype) == 0 || num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        num_heads % num_kv_heads != 0 || partition_tokens < 0 ||
+        (partition_tokens > 0 &&
+         (partition_tokens % kBlock != 0 || partition_tokens > kMaxPartition)) ||
+        (flags & ~(PA_DECODE_SHARED_BLOCKS | PA_DECODE_FORCE_VALU | PA_DECODE_MERGE_KERNEL))) {
+        fail(PA_ERR_INVALID_ARG, "pa_decode_merge_mode: bad arguments");
+        return -PA_ERR_INVALID_ARG;
+    }
+    if (num_seqs == 0) return PA_MERGE_NONE;
+    const pa::DecodeShape sh = pa::decode_shape(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_blocks_per_seq, dtype,
+                                                partition_tokens, flags);
+    if (sh.NP <= 1) return PA_MERGE_NONE;
+    return sh.fused && xcd_rule_holds(false) ? PA_MERGE_IN_KERNEL : PA_MERGE_KERNEL;
+}
 
 int pa_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                  const int32_t *block_tables, const int32_t *context_lens, float scale,
@@ -827,7 +998,7 @@ int pa_release_workspaces(void) {
     (void)hipGetDevice(&prev);
     for (auto it = g_ws.begin(); it != g_ws.end();) {
         Workspace &w = it->second;
-        (void)hipSetDevice(it->first.first);
+        (void)hipSetDevice(std::get<0>(it->first));
         hipError_t e = hipDeviceSynchronize();
         if (e != hipSuccess) {  // keep the buffers: work may still use them
             rc = hip_fail(e, "pa_release_workspaces");

@@ -42,6 +42,7 @@ enum : unsigned {
     kBadQueryStart = 128u, // query_start not 0 .. num_tokens non-decreasing, or a chunk
                            // longer than its context or than max_query_len
     kBadGroup = 256u,      // group_start / prefix_blocks inconsistent with the sequences
+    kXcdSplit = 512u,      // the units of one split row ran on more than one XCD
 };
 
 const char *const kFlagText[] = {
@@ -55,6 +56,8 @@ const char *const kFlagText[] = {
     "query_start is not non-decreasing from 0 to num_tokens, or a chunk is longer than its "
     "context or than max_query_len",
     "group_start / prefix_blocks do not describe consecutive groups sharing their prefix blocks",
+    "the work units of one (sequence, kv head) ran on more than one XCD, so the in-kernel merge "
+    "of that call may have read stale partials; pass PA_DECODE_MERGE_KERNEL on this device",
 };
 
 __device__ __forceinline__ void raise(unsigned *flags, unsigned bit) { atomicOr(flags, bit); }
@@ -160,6 +163,11 @@ __global__ void check_groups_kernel(const int32_t *gs, const int32_t *pblk, cons
             }
         }
     }
+}
+
+__global__ void check_xcd_kernel(const unsigned *seen, int64_t rows, unsigned *flags) {
+    for (int64_t r = gtid(); r < rows; r += gstride())
+        if (__popc(seen[r]) > 1) raise(flags, kXcdSplit);
 }
 
 int grid_for(int64_t n) {
@@ -307,6 +315,17 @@ int debug_check_groups(const char *who, const int32_t *gs, const int32_t *pblk, 
     if (rc != PA_OK) return rc;
     check_groups_kernel<<<grid_for((int64_t)NG * (MB > 0 ? MB : 1)), 256, 0, stream>>>(
         gs, pblk, bt, ctx, NG, S, MB, max_group, flags);
+    return finish(who, stream, sc);
+}
+
+int debug_check_xcd(const char *who, const unsigned *seen, int64_t rows, hipStream_t stream,
+                    unsigned *flags_buf) {
+    if (rows <= 0) return PA_OK;
+    Scratch sc;
+    unsigned *flags, *bm;
+    int rc = begin(who, stream, 0, sc, &flags, &bm, flags_buf);
+    if (rc != PA_OK) return rc;
+    check_xcd_kernel<<<grid_for(rows), 256, 0, stream>>>(seen, rows, flags);
     return finish(who, stream, sc);
 }
 

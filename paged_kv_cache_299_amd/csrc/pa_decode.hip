@@ -11,10 +11,11 @@
 // Work unit = (sequence, partition p, kv head or query head), one wave64 per
 // unit.  A sequence longer than P tokens is cut into the fewest partitions of
 // at most P tokens, equal in whole blocks (blocks_per_partition); each
-// writes (m, l, unnormalised o) and merge_kernel recombines the partitions with
+// writes (m, l, unnormalised o), and the partitions are recombined with
 // log-sum-exp weights -- the streaming softmax is associative, so the split
-// only changes rounding.  A sequence that fits one partition is normalised and
-// written by its single unit directly.
+// only changes rounding -- either inside the partition kernel by the row's
+// last unit (merge_row_in_l2) or by a merge kernel after it.  A sequence that
+// fits one partition is normalised and written by its single unit directly.
 //
 // Two partition kernels:
 //  * decode_mfma_kernel (bf16/fp16, 1..16 query heads per kv head): the G
@@ -32,6 +33,8 @@
 // as 16-byte (K) and 8/16-byte (V) loads that cover the tile in order, and
 // keep one block requested ahead of the one being reduced.
 #include <math.h>
+
+#include <vector>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -102,6 +105,109 @@ __device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups
         base += total;
     }
     return false;
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the partitions of one (sequence, query head):
+//   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise,
+// over the partitions q = 0 .. np - 1 in order; out = o / L.  Every merge
+// here folds the partitions in this order, so the in-kernel merge and the
+// merge kernels give the same bits.
+// ---------------------------------------------------------------------------
+struct LseState {
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // fold in a partition (m_q finite: every partition has a token)
+    __device__ __forceinline__ void add(float mq, float lq, const f32x4 &oq) {
+        const float Mn = fmaxf(M, mq);
+        const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
+        L = L * ca + lq * cb;
+        acc = acc * ca + oq * cb;
+        M = Mn;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// In-kernel merge of a split row (matrix-core kernel).
+//
+// Row (s, g) = sequence s, kv head g, cut into npart partitions.  With Hkv a
+// multiple of 8, the row's units are workgroups b = base_s + p Hkv + g
+// (base_s a multiple of Hkv), all congruent to g mod 8; the dispatcher deals
+// workgroup b to XCD (b + r) mod 8 (probe_xcd_dispatch checks this once per
+// device), so one XCD runs all of them, and its L2 is their point of
+// coherence.  Each unit has stored its partial with plain stores (the L1 writes
+// through); it waits until the L2 has them all, then adds one to the row's
+// counter with an L2 atomic.  The unit that draws npart - 1 is the last: it
+// zeroes the counter for the next call, reads the npart partials of the G
+// heads with L1-bypassing (sc0) loads in one round trip, and writes the
+// outputs.  Nobody waits for anybody.  No cross-XCD coherence is needed, so
+// no L2 write-back or invalidate is issued: a device-scope version of the
+// same protocol (sc1 stores, loads and atomic) made the Llama-3-8B-shaped step
+// slower than a separate merge kernel, this one makes it 1.2-2 us faster.
+// The host takes this path only when all units are resident at once (a unit
+// that holds its slot through the ticket round trip would delay the units
+// queued behind it) and rows have at most kFusedMaxParts partitions.
+// ---------------------------------------------------------------------------
+constexpr int kL1Bypass = 1;  // sc0 on a buffer load: served by the L2, not the L1
+
+__device__ __forceinline__ unsigned xcc_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15u;  // hwreg(XCC_ID, 0, 4)
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void merge_row_in_l2(const DecodeArgs &a, int s, int g, int npart) {
+    const int lane = threadIdx.x;
+    const int64_t row = (int64_t)s * a.Hkv + g;
+    if (a.xcd_seen && lane == 0)  // PA_DEBUG: which XCDs ran the row's units
+        __hip_atomic_fetch_or(a.xcd_seen + row, 1u << xcc_id(), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    // this wave's partial is in the L2 before its ticket
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int t = 0;
+    if (lane == 0)
+        t = __hip_atomic_fetch_add(a.ticket + row, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t != npart - 1) return;
+    if (lane == 0) a.ticket[row] = 0;
+
+    // the G * D outputs of the row as f32x4 pieces: piece k = lane + 64 i is
+    // head k / (D / 4), dims 4 (k % (D / 4)) .. + 3 (the host takes this path
+    // only for G * D <= 512)
+    const int G = a.G;
+    const int items = G * (D / 4);
+    const int64_t h0 = (int64_t)s * a.Hq + g * G;  // first query head of the row
+    const auto ro = tile_rsrc((const char *)(a.part_o + h0 * a.NP * D), G * a.NP * D * 4);
+    const auto rml = tile_rsrc((const char *)(a.part_ml + h0 * a.NP * 2), G * a.NP * 8);
+    constexpr int kNone = 0x7ffffff0;  // outside the descriptor: no request
+    f32x4 ov[2][kFusedMaxParts];
+    f32x2 mlv[2][kFusedMaxParts];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = lane + 64 * i;
+        const int hh = k / (D / 4);
+        const int d0 = 4 * (k % (D / 4));
+#pragma unroll
+        for (int q = 0; q < kFusedMaxParts; ++q) {
+            const bool in = k < items && q < npart;
+            ov[i][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                ro, in ? ((hh * a.NP + q) * D + d0) * 4 : kNone, 0, kL1Bypass));
+            mlv[i][q] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                rml, in ? (hh * a.NP + q) * 8 : kNone, 0, kL1Bypass));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = lane + 64 * i;
+        if (k >= items) continue;
+        const int hh = k / (D / 4);
+        const int d0 = 4 * (k % (D / 4));
+        LseState st;
+#pragma unroll
+        for (int q = 0; q < kFusedMaxParts; ++q)
+            if (q < npart) st.add(mlv[i][q][0], mlv[i][q][1], ov[i][q]);
+        store4<DT>((char *)a.out + ((h0 + hh) * D + d0) * Elem<DT>::bytes, st.acc, 1.f / st.L);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -358,18 +464,21 @@ void decode_mfma_kernel(const DecodeArgs a) {
             for (int e = 0; e < 4; ++e) o[t][e] += __shfl_down(o[t][e], a.G, 16);
     }
     const float lt = xor32_sum(xor16_sum(l));  // all lanes take part in the swaps
-    if (!hi_col) return;
     if (t0 == 0 && t1 == ctx) {  // the unit covers the whole context
+        if (!hi_col) return;
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < NVT; ++t) store4<DT>(outp + 16 * t + 4 * j, o[t], inv);
         return;
     }
-    const int64_t part = ((int64_t)s * a.Hq + h) * a.NP + p;
-    float *po = a.part_o + part * D;
+    if (hi_col) {
+        const int64_t part = ((int64_t)s * a.Hq + h) * a.NP + p;
+        float *po = a.part_o + part * D;
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
-    if (j == 0) *(float2 *)(a.part_ml + 2 * part) = float2{m, lt};
+        for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
+        if (j == 0) *(float2 *)(a.part_ml + 2 * part) = float2{m, lt};
+    }
+    if (a.fuse_merge) merge_row_in_l2<DT, D>(a, s, g, (ctx + a.P - 1) / a.P);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,10 +957,9 @@ hipError_t launch_read_tiles(const DecodeArgs &a, int head_dim, int *sink, hipSt
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one (sequence, query head):
-//   M' = max(M, m_q),  L' = L 2^(M-M') + l_q 2^(m_q-M'),  o' likewise,
-// over the partitions q = 0 .. np - 1 in order, np following from the context
-// length; out = o / L.
+// Merge kernels: the log-sum-exp merge (LseState) of every split row, run
+// after the partition kernel when the in-kernel merge does not apply; np
+// follows from the context length.
 //
 // merge_kernel (rows of at most 16 partitions): D/4 lanes per row, four dims
 // each.  The (m, l, o) of the first kSpec = 2 partitions are requested
@@ -873,19 +981,6 @@ hipError_t launch_read_tiles(const DecodeArgs &a, int head_dim, int *sink, hipSt
 constexpr int kMergeThreads = 128;   // 4 rows at D = 128
 constexpr int kMergeWideThreads = 256;
 constexpr int kMergeWideMaxParts = 16;  // rows with more partitions take the wide merge
-
-struct LseState {
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // fold in a partition (m_q finite: every partition has a token)
-    __device__ __forceinline__ void add(float mq, float lq, const f32x4 &oq) {
-        const float Mn = fmaxf(M, mq);
-        const float ca = fast_exp2(M - Mn), cb = fast_exp2(mq - Mn);
-        L = L * ca + lq * cb;
-        acc = acc * ca + oq * cb;
-        M = Mn;
-    }
-};
 
 template <int DT, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a) {
@@ -1031,7 +1126,7 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.NP > 1 && a.S > 0) {
+    if (a.NP > 1 && a.S > 0 && !a.fuse_merge) {
         const int rows = a.S * a.Hq;
         if (a.NP > kMergeWideMaxParts) {
             merge_wide_kernel<DT, D><<<dim3(rows), dim3(kMergeWideThreads), 0, stream>>>(a);
@@ -1058,6 +1153,51 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, DecodeKer
         return head_dim == 64 ? launch_typed<kBF16, 64>(a, kind, stream)
                               : launch_typed<kBF16, 128>(a, kind, stream);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch probe for the in-kernel merge: each workgroup records the XCD it
+// runs on.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void xcd_probe_kernel(unsigned *xcd) {
+    if (threadIdx.x == 0) xcd[blockIdx.x] = xcc_id();
+}
+
+hipError_t probe_xcd_dispatch(int *num_xcd, bool *ok) {
+    constexpr int kWorkgroups = 4096;
+    *num_xcd = 0;
+    *ok = false;
+    unsigned *d = nullptr;
+    hipError_t e = hipMalloc(&d, kWorkgroups * sizeof(unsigned));
+    if (e != hipSuccess) return e;
+    hipStream_t st = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    std::vector<unsigned> h(kWorkgroups, ~0u);
+    if (e == hipSuccess) {
+        xcd_probe_kernel<<<kWorkgroups, 64, 0, st>>>(d);
+        e = hipGetLastError();
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(h.data(), d, kWorkgroups * sizeof(unsigned),
+                               hipMemcpyDeviceToHost, st);
+        const hipError_t e2 = hipStreamSynchronize(st);
+        if (e == hipSuccess) e = e2;
+        (void)hipStreamDestroy(st);
+    }
+    (void)hipFree(d);
+    if (e != hipSuccess) return e;
+    // X distinct ids in the first X workgroups, then the same cycle throughout
+    int X = 0;
+    while (X < 16 && X < kWorkgroups) {
+        bool seen = false;
+        for (int i = 0; i < X; ++i) seen |= h[i] == h[X];
+        if (seen) break;
+        ++X;
+    }
+    bool cyclic = X >= 1 && X <= 16;
+    for (int b = X; cyclic && b < kWorkgroups; ++b) cyclic = h[b] == h[b % X];
+    *num_xcd = X;
+    *ok = cyclic;
+    return hipSuccess;
 }
 
 }  // namespace pa

@@ -35,13 +35,31 @@ struct DecodeArgs {
     // K/V ([S][Hkv][D]) are stored into its slot by the unit that reads it.
     const void *k_new;
     const void *v_new;
+    // In-kernel merge of split rows (matrix-core kernel, B = 8 or 16): the
+    // unit of a row that finishes last merges the row's partials through the
+    // L2 of the XCD that ran all of the row's units (merge_row_in_l2).
+    int fuse_merge;
+    int *ticket;            // [S][Hkv] finished-unit counters, zero between calls
+    unsigned *xcd_seen;     // PA_DEBUG: [S][Hkv] bit x set by each unit run on XCD x, or null
 };
+
+// In-kernel merge limits: partitions per row, and work units per launch
+// (all resident at once).
+constexpr int kFusedMaxParts = 8;
+constexpr int64_t kFusedMaxUnits = 2048;
 
 enum class DecodeKernel { kValu, kMfma };
 
-// Launch the partition kernel (and, when NP > 1, the merge kernel).
+// Launch the partition kernel (and, when NP > 1 without fuse_merge, the merge kernel).
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, DecodeKernel kind,
                          hipStream_t stream);
+
+// Workgroup b of a launch runs on the XCD numbered (b + r) mod X for some r,
+// where X is the number of XCDs: checked once per device by a probe launch of
+// 4,096 workgroups that read their XCD's id (the hardware dispatcher deals
+// workgroups to the XCDs in turn).  Writes the XCD count to *num_xcd and
+// whether the rule held to *ok; the probe runs on its own stream and is waited for.
+hipError_t probe_xcd_dispatch(int *num_xcd, bool *ok);
 
 // Loads only: the K/V tiles the matrix-core partition kernel would read for
 // these arguments (16-bit data, B = 16), for measuring the access pattern.
@@ -139,5 +157,9 @@ int debug_check_query_start(const char *who, const int32_t *qs, const int32_t *c
 int debug_check_groups(const char *who, const int32_t *gs, const int32_t *pblk, const int32_t *bt,
                        const int32_t *ctx, int NG, int S, int MB, int max_group,
                        hipStream_t stream);
+// After a decode with the in-kernel merge: every row's units ran on one XCD
+// (`seen`: the kernel's [rows] XCD bit sets, zeroed before it; flags_buf as above).
+int debug_check_xcd(const char *who, const unsigned *seen, int64_t rows, hipStream_t stream,
+                    unsigned *flags_buf = nullptr);
 
 }  // namespace pa

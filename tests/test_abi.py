@@ -74,7 +74,7 @@ def _decode(lib, **kw):
     (dict(scale=float("inf")), INVALID),
     (dict(P=20), INVALID),
     (dict(P=2048), INVALID),
-    (dict(flags=4), INVALID),
+    (dict(flags=8), INVALID),
     (dict(flags=2, B=32), UNSUPPORTED),          # the VALU kernel takes 16-token blocks
     (dict(B=24), UNSUPPORTED),
     (dict(B=32, dtype=F32), UNSUPPORTED),        # block sizes 8 / 32: matrix-core kernel only
@@ -361,3 +361,30 @@ def test_noalloc_rejects_a_workspace_past_its_static_array():
     # allocate (not called here past its checks: num_seqs = 0 returns first)
     assert lib.pa_decode_noalloc(A, A, A, A, A, 0.1, A, 0, 32, 8, 128, 16, 65536, 100, BF16, 16,
                                  0, None) == OK
+
+
+def test_merge_mode_query():
+    """pa_decode_merge_mode: argument checks, and the cases that need no device."""
+    import torch
+    lib = pa.load_library()
+    # bad arguments: -(status)
+    assert lib.pa_decode_merge_mode(4, 32, 8, 128, 16, 10, 9, 0, 0) == -INVALID   # dtype
+    assert lib.pa_decode_merge_mode(4, 30, 8, 128, 16, 10, BF16, 0, 0) == -INVALID  # Hq % Hkv
+    assert lib.pa_decode_merge_mode(4, 32, 8, 128, 16, 10, BF16, 24, 0) == -INVALID  # P
+    assert lib.pa_decode_merge_mode(4, 32, 8, 128, 16, 10, BF16, 0, 8) == -INVALID  # flags
+    with pytest.raises(ValueError):
+        pa.pa_decode_merge_mode(4, 32, 8, 128, 16, 10, torch.bfloat16, partition_tokens=24)
+    # tables of 160 tokens fit one partition; no sequences; the merge kernel asked for
+    assert pa.pa_decode_merge_mode(4, 32, 8, 128, 16, 10, torch.bfloat16) == pa.PA_MERGE_NONE
+    assert pa.pa_decode_merge_mode(0, 32, 8, 128, 16, 256, torch.bfloat16, 256) == \
+        pa.PA_MERGE_NONE
+    assert pa.pa_decode_merge_mode(32, 32, 8, 128, 16, 256, torch.bfloat16, 640,
+                                   merge_kernel=True) == pa.PA_MERGE_KERNEL
+    # no in-kernel merge for: more than 8 partitions; kv heads not a multiple of 8;
+    # fp32 (VALU kernel); block size 32; more than 2,048 units
+    for args in [(32, 32, 8, 128, 16, 256, torch.bfloat16, 256),
+                 (32, 32, 4, 128, 16, 256, torch.bfloat16, 640),
+                 (32, 32, 8, 128, 16, 256, torch.float32, 640),
+                 (32, 32, 8, 128, 32, 128, torch.bfloat16, 640),
+                 (64, 32, 8, 128, 16, 256, torch.bfloat16, 640)]:
+        assert pa.pa_decode_merge_mode(*args) == pa.PA_MERGE_KERNEL, args
