@@ -258,13 +258,20 @@ def main():
     NB, dt = case.num_blocks, case.dtype
     e = ELEM_BYTES[dt]
     part = args.partition if args.partition is not None else (case.partition_tokens or 0)
-    # no length given: plan it from the batch's context lengths on the host, as
-    # the scheduler that built the batch would (pa_decode_plan; 0 = automatic)
+    # No length given: plan it from the batch's context lengths on the host, as
+    # the scheduler that built the batch would (pa_decode_plan; 0 = automatic),
+    # and time the plain pa_decode beside it: its automatic split plans the
+    # length on the device from the same lengths by the same rule where it can
+    # (matrix-core kernel at B = 16, fewer than 2,048 rows, at most 256
+    # sequences, tables of 513 to 2^20 tokens).
+    mfma = dt != torch.float32 and Hq // Hkv <= 16 and not args.force_valu
     planned = False
     if args.partition is None and not case.partition_tokens and not args.cascade \
             and not args.force_valu:
         part = pa.pa_decode_plan(case.context_lens, Hq, Hkv, B, case.max_blocks, dt)
         planned = part > 0
+    device_plan = (mfma and B == 16 and S * Hkv < 2048 and S <= 256
+                   and 512 < case.max_blocks * B <= (1 << 20) and not args.cascade)
     k_shape, v_shape = kv_cache_shapes(NB, Hkv, D, B, dt)
     gen = torch.Generator(device=dev)
     pools = []
@@ -347,11 +354,12 @@ def main():
                          shared_blocks=shared, force_valu=args.force_valu)
 
     # eager warmup on the capture stream (grows the library's workspace for it;
-    # the plain pa_decode phase below may need a larger one than `part`)
+    # the plain pa_decode phase below may need another size than `part`)
+    time_plain = planned and not append
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             enqueue(i % L)
-        if part and not args.cascade and not append and not args.force_valu:
+        if time_plain:
             enqueue(0, plain=True)
     torch.cuda.synchronize()
 
@@ -427,10 +435,9 @@ def main():
         _, wr_ms = timed(args.steps, decode=False)
         wr_avg = wr_ms / args.steps
     dec_spread = spread(write=False)
-    # plain pa_decode (the library's automatic partition length) beside the
-    # planned length the headline uses, when they differ
+    # the plain pa_decode (its automatic split) beside the host-planned length
     plain_us = None
-    if part and not args.cascade and not append and not args.force_valu:
+    if time_plain:
         _, pl_ms = timed(args.steps, plain=True)
         plain_us = pl_ms / args.steps * 1e3
     read_us = None
@@ -518,7 +525,8 @@ def main():
         "append_us": round(app_avg * 1e3, 2) if append else None,
         "decode_entry": ("pa_decode_cascade" if args.cascade
                          else "pa_decode_append" if append
-                         else f"pa_decode_ex (partition_tokens {part})" if part or shared
+                         else f"pa_decode_ex (partition_tokens {part})"
+                         if part or shared or args.force_valu
                          else "pa_decode"),
         "merge": (None if args.cascade else
                   {0: "none (one partition per table)", 1: "merge kernel",
@@ -542,7 +550,10 @@ def main():
                      "bytes_per_launch": int(roof_bytes)},
         "effective_GBps": round(dec_bytes / (dec_avg * 1e-3) / 1e9, 2),
         "decode_plain": None if plain_us is None else {
-            "entry": "pa_decode (automatic partition length)", "us": round(plain_us, 2),
+            "entry": "pa_decode (automatic partitions: " + (
+                "length planned on the device from the context lengths)" if device_plan
+                else "the library's length for the table size)"),
+            "us": round(plain_us, 2),
             "GBps": round(roof_bytes / (plain_us * 1e-6) / 1e9, 2),
             "frac_of_peak": round(roof_bytes / (plain_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
         # the decode's K/V loads alone (pa_read_tiles: same units, load

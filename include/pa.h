@@ -99,8 +99,14 @@ int pa_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cac
  *   out            [num_seqs][num_heads][head_dim], device, written
  *
  * Long contexts are split into partitions whose partial results are merged
- * with log-sum-exp weights; the library keeps a grow-only workspace for them
- * per (device, stream) (PA_ERR_NO_MEMORY if it cannot be allocated).  A
+ * with log-sum-exp weights.  The partition length is automatic: with bf16 /
+ * fp16 data, at most 16 query heads per kv head, block_size 16, fewer than
+ * 2,048 (sequence, kv head) rows, at most 256 sequences and tables of 513 to
+ * 2^20 tokens, the kernels choose it on the device from context_lens by the
+ * rule of pa_decode_plan (same length, same bits as pa_decode_ex with the
+ * length pa_decode_plan gives for the same lengths); otherwise it follows
+ * from the sizes alone.  The library keeps a grow-only workspace for the
+ * partials per (device, stream) (PA_ERR_NO_MEMORY if it cannot be allocated).  A
  * workspace buffer is never freed before pa_release_workspaces, so a HIP graph
  * that captured pa_decode stays valid; the first call on a stream that needs
  * a larger workspace allocates one (hipMalloc), so make that call before
@@ -497,7 +503,8 @@ int pa_decode_merge_mode(int num_seqs, int num_heads, int num_kv_heads, int head
                          int block_size, int max_blocks_per_seq, int dtype,
                          int partition_tokens, int flags);
 
-/* Bytes of workspace pa_decode_ex would use for these sizes (0 = none). */
+/* Bytes of workspace pa_decode_ex would use for these sizes (0 = none); for
+ * partition_tokens 0, an upper bound over the automatic choices. */
 int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int block_size,
                                   int max_blocks_per_seq, int partition_tokens);
 

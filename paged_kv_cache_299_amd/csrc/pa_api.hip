@@ -466,10 +466,12 @@ int64_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int
         return 0;
     const int max_tokens = max_blocks_per_seq * block_size;
     // an upper bound: the smallest partition length the library picks itself
+    // (plus the 256 bytes a length planned on the device keeps beside them)
     int P = partition_tokens > 0 ? partition_tokens : 256;
     if (P >= max_tokens) return 0;
     const int64_t np = num_partitions(max_tokens, P);
-    return (int64_t)num_seqs * num_heads * np * (head_dim + 2) * (int64_t)sizeof(float);
+    return (int64_t)num_seqs * num_heads * np * (head_dim + 2) * (int64_t)sizeof(float) +
+           (partition_tokens > 0 ? 0 : 256);
 }
 
 }  // extern "C"
@@ -483,7 +485,19 @@ struct DecodeShape {
     int64_t NP;      // partitions per row for full tables
     int64_t units;   // work units for full tables (the grid)
     bool fused;      // merge inside the partition kernel (subject to the dispatch probe)
+    bool plan;       // P chosen on the device (device_plan); P, NP, units: for 512 tokens
 };
+
+// Automatic partitions planned on the device from the context lengths: the
+// matrix-core kernel at B = 16 with fewer than 2,048 rows (sequences x kv
+// heads; more rows fill the machine at 256 tokens), at most 256 sequences
+// (every workgroup holds all context lengths in four registers), and tables
+// longer than the shortest candidate (512 tokens; shorter ones take one pass
+// anyway) and of at most 2^20 tokens (the plan's integer quotients go
+// through fp32).
+constexpr int kPlanMaxSeqs = 256;
+constexpr int kPlanShortest = 512;
+constexpr int kPlanLongest = 1 << 20;
 
 DecodeShape decode_shape(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                          int block_size, int max_blocks_per_seq, int dtype,
@@ -494,7 +508,11 @@ DecodeShape decode_shape(int num_seqs, int num_heads, int num_kv_heads, int head
     // block size 8: a unit's table slice is 64 entries = 512 tokens
     const int max_part = block_size == 8 ? 512 : kMaxPartition;
     sh.mfma = dtype != PA_F32 && G <= 16 && !(flags & PA_DECODE_FORCE_VALU);
-    int P = partition_tokens > 0
+    sh.plan = partition_tokens == 0 && sh.mfma && block_size == kBlock &&
+              (int64_t)num_seqs * num_kv_heads < 2048 && num_seqs <= kPlanMaxSeqs &&
+              max_tokens > kPlanShortest && max_tokens <= kPlanLongest;
+    int P = sh.plan ? kPlanShortest
+            : partition_tokens > 0
                 ? partition_tokens
                 : std::min(auto_partition(sh.mfma,
                                           (int64_t)num_seqs * (sh.mfma ? num_kv_heads : num_heads),
@@ -621,6 +639,8 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
     a.MB = max_blocks_per_seq;
     a.NP = (int)NP;
     a.P = P;
+    a.plan = sh.plan ? 1 : 0;
+    a.cus = device_cus();
     a.NB = num_blocks;
     a.BS = block_size;
     a.num_units = (int)units;
@@ -634,8 +654,11 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         a.req_stride = contig->req_stride;
         a.num_req = contig->num_req;
     }
+    // a planned launch keeps its length after the partials, for the merge kernel
+    const size_t plan_bytes = sh.plan ? 256 : 0;
     const size_t part_bytes =
-        NP > 1 ? (size_t)num_seqs * num_heads * NP * (head_dim + 2) * sizeof(float) : 0;
+        NP > 1 ? (size_t)num_seqs * num_heads * NP * (head_dim + 2) * sizeof(float) + plan_bytes
+               : 0;
     void *fixed = nullptr;  // pa_decode_noalloc: the static scratch
     if (no_alloc) {
         if (part_bytes > kScratchBytes - kScratchPartials)
@@ -672,6 +695,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache,
         }
         a.part_o = (float *)ws;
         a.part_ml = (float *)((char *)ws + o_bytes);
+        if (sh.plan) a.plan_slot = (int *)((char *)ws + part_bytes - plan_bytes);
         if (sh.fused) {
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             hipError_t ce = hipStreamIsCapturing((hipStream_t)stream, &cs);

@@ -74,9 +74,9 @@ __device__ __forceinline__ int table_entry(const DecodeArgs &a, int s, int blk) 
     return a.req[s] * a.req_stride + blk;  // only read when seq_ctx(s) > 0: r in range
 }
 
-__device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups, int &s_out,
-                                          int &ctx_out, int &r_out) {
-    const int S = a.S, P = a.P;
+__device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int P, int groups,
+                                          int &s_out, int &ctx_out, int &r_out) {
+    const int S = a.S;
     const int lane = threadIdx.x & 63;
     int base = 0;
     for (int c0 = 0; c0 < S; c0 += 64) {
@@ -105,6 +105,142 @@ __device__ __forceinline__ bool find_unit(int b, const DecodeArgs &a, int groups
         base += total;
     }
     return false;
+}
+
+// ---------------------------------------------------------------------------
+// Partition length planned on the device (DecodeArgs::plan: automatic
+// partitions of the matrix-core kernel at B = 16 with fewer than 2,048 rows,
+// at most 256 sequences and tables of at most 2^20 tokens).  Every unit of
+// the split is resident at once, so a compute unit runs about ceil(units /
+// CUs) of them and the call lasts about as long as that many of the longest;
+// of 512, 640, ..., 1024 tokens the length that makes this product smallest is
+// taken, ties to the longer (fewer partials to merge) -- the rule
+// pa_decode_plan applies on the host, here to the context lengths the kernels
+// read anyway.  Each wave computes it for itself from one load of the lengths
+// (sequences lane, 64 + lane, 128 + lane, 192 + lane), and all get the same
+// value; all 64 lanes must be active.
+// ---------------------------------------------------------------------------
+constexpr int kPlanChunks = 4;       // 256 sequences
+constexpr int kPlanCandidates = 5;   // 512, 640, ..., 1024 tokens
+
+// t / d for t < 2^24 and t / d < 2^21: the quotient through the float
+// reciprocal is off by at most one, and one step corrects it.
+__device__ __forceinline__ unsigned udiv_small(unsigned t, unsigned d) {
+    unsigned q = (unsigned)((float)t * __builtin_amdgcn_rcpf((float)d));
+    const int rem = (int)(t - q * d);
+    return rem < 0 ? q - 1 : (rem >= (int)d ? q + 1 : q);
+}
+
+// Context lengths of this lane's sequences (-1: no sequence).
+__device__ __forceinline__ void plan_lengths(const DecodeArgs &a, int (&c)[kPlanChunks]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kPlanChunks; ++i) {
+        const int s = 64 * i + lane;
+        c[i] = -1;
+        if (64 * i < a.S && s < a.S) c[i] = seq_ctx(a, s);
+    }
+}
+
+// Units at 512 tokens, summed over the wave (x groups): no candidate makes more.
+__device__ __forceinline__ int plan_max_units(const DecodeArgs &a, const int (&c)[kPlanChunks],
+                                              int groups) {
+    int u = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanChunks; ++i) {
+        if (64 * i >= a.S) break;  // (uniform)
+        u += c[i] < 0 ? 0 : (c[i] > 512 ? (c[i] + 511) >> 9 : 1);
+    }
+    return __builtin_amdgcn_readfirstlane(wave_sum_i32(u)) * groups;
+}
+
+__device__ __forceinline__ int plan_choose(const DecodeArgs &a, const int (&c)[kPlanChunks],
+                                           int units512) {
+    unsigned units[kPlanCandidates], longest[kPlanCandidates];
+#pragma unroll
+    for (int k = 0; k < kPlanCandidates; ++k) units[k] = 0, longest[k] = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanChunks; ++i) {
+        if (64 * i >= a.S) break;  // (uniform)
+        const bool in = c[i] >= 0;
+        const unsigned cc = in ? (unsigned)c[i] : 0u;
+        const unsigned nb = (cc + kB - 1) / kB;
+#pragma unroll
+        for (int k = 0; k < kPlanCandidates; ++k) {
+            const unsigned P = 512 + 128 * k;
+            const unsigned np = cc > P ? (cc + P - 1) / P : 1u;
+            if (k > 0) units[k] += in ? np : 0u;
+            longest[k] = max(longest[k], udiv_small(nb + np - 1, np));  // ceil(nb / np)
+        }
+    }
+    int best = 0;
+    unsigned best_cost = ~0u;
+#pragma unroll
+    for (int k = 0; k < kPlanCandidates; ++k) {
+        // units * Hkv < 2^22 (fewer than 2,048 rows of at most 2,048 partitions)
+        const unsigned u = k == 0 ? (unsigned)units512
+                                  : (unsigned)wave_sum_i32((int)units[k]) * (unsigned)a.Hkv;
+        const unsigned lg = (unsigned)wave_max_i32((int)longest[k]);
+        const unsigned cost = udiv_small(u + a.cus - 1, a.cus) * lg;
+        if (cost <= best_cost) best_cost = cost, best = 512 + 128 * k;
+    }
+    return __builtin_amdgcn_readfirstlane(best);
+}
+
+// The partition length of a merge kernel's launch: a planned one reads what
+// the partition kernel before it chose (its workgroup 0 stores it).
+__device__ __forceinline__ int merge_partition_len(const DecodeArgs &a) {
+    return a.plan ? *a.plan_slot : a.P;
+}
+
+// Unit search of a planned launch: the lengths are loaded once; workgroups
+// past the units at 512 tokens (no candidate makes more) leave before the
+// plan -- tables far longer than the contexts leave most of the grid, which
+// is sized for full tables at 512, without a unit; then the plan, then the
+// b-th unit at the chosen length, as find_unit.
+__device__ __forceinline__ bool plan_find_unit(int b, const DecodeArgs &a, int groups, int &P_out,
+                                               int &s_out, int &ctx_out, int &r_out) {
+    const int lane = threadIdx.x & 63;
+    int c[kPlanChunks];
+    plan_lengths(a, c);
+    const int u512 = plan_max_units(a, c, groups);
+    if (b >= u512) return false;
+    const int P = plan_choose(a, c, u512);
+    P_out = P;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanChunks; ++i) {
+        if (64 * i >= a.S) break;
+        const int ci = c[i];
+        const int u = ci < 0 ? 0
+                             : groups * (ci > P ? (int)udiv_small((unsigned)(ci + P - 1),
+                                                                  (unsigned)P) : 1);
+        int incl = u;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (b < base + total) {
+            const uint64_t past = __ballot(base + incl > b);
+            const int first = __builtin_amdgcn_readfirstlane(__builtin_ctzll(past));
+            s_out = 64 * i + first;
+            ctx_out = __builtin_amdgcn_readlane(ci, first);
+            r_out = b - (base + __builtin_amdgcn_readlane(incl - u, first));
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// The unit of workgroup b and the partition length, planned or not.
+__device__ __forceinline__ bool unit_of(int b, const DecodeArgs &a, int groups, int &P, int &s,
+                                        int &ctx, int &r) {
+    if (a.plan) return plan_find_unit(b, a, groups, P, s, ctx, r);
+    P = a.P;
+    return find_unit(b, a, P, groups, s, ctx, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -266,11 +402,12 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
-    int s, ctx, r;
-    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
+    int P, s, ctx, r;
+    if (!unit_of(blockIdx.x, a, a.Hkv, P, s, ctx, r)) return;
+    if (a.plan && blockIdx.x == 0 && lane == 0) *a.plan_slot = P;  // for the merge kernel
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
-    const int per = blocks_per_partition(ctx, a.P);
+    const int per = blocks_per_partition(ctx, P);
     const int blk0 = p * per;  // in steps of 16 tokens
     const int t0 = blk0 * kB;
     const int e0 = t0 / BS;    // the unit's first table entry
@@ -478,7 +615,7 @@ void decode_mfma_kernel(const DecodeArgs a) {
         for (int t = 0; t < NVT; ++t) *(f32x4 *)(po + 16 * t + 4 * j) = o[t];
         if (j == 0) *(float2 *)(a.part_ml + 2 * part) = float2{m, lt};
     }
-    if (a.fuse_merge) merge_row_in_l2<DT, D>(a, s, g, (ctx + a.P - 1) / a.P);
+    if (a.fuse_merge) merge_row_in_l2<DT, D>(a, s, g, (ctx + P - 1) / P);
 }
 
 // ---------------------------------------------------------------------------
@@ -502,7 +639,7 @@ void decode_mfma_b32_kernel(const DecodeArgs a) {
     const int n = lane & 15;
     const int j = lane >> 4;
     int s, ctx, r;
-    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
+    if (!find_unit(blockIdx.x, a, a.P, a.Hkv, s, ctx, r)) return;
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
     // ceil(ctx / P) partitions of equal whole blocks (ceil(nb / per) of them are
@@ -764,7 +901,7 @@ void decode_valu_kernel(const DecodeArgs a) {
     // Units in the order of find_unit (sequence-major, head fastest).  With a
     // multiple of 8 heads, head h of a sequence runs on XCD (offset + h) % 8.
     int s, ctx, r;
-    if (!find_unit(blockIdx.x, a, a.Hq, s, ctx, r)) return;
+    if (!find_unit(blockIdx.x, a, a.P, a.Hq, s, ctx, r)) return;
     const int h = r % a.Hq;
     const int p = r / a.Hq;
     const int g = h / a.G;
@@ -897,12 +1034,12 @@ __global__ __launch_bounds__(64) void read_tiles_kernel(const DecodeArgs a, int 
     const int lane = threadIdx.x;
     const int n = lane & 15;
     const int j = lane >> 4;
-    int s, ctx, r;
-    if (!find_unit(blockIdx.x, a, a.Hkv, s, ctx, r)) return;
+    int P, s, ctx, r;
+    if (!unit_of(blockIdx.x, a, a.Hkv, P, s, ctx, r)) return;
     if (ctx == 0) return;
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
-    const int per = blocks_per_partition(ctx, a.P);
+    const int per = blocks_per_partition(ctx, P);
     const int t0 = p * per * kB;
     const int t1 = min(ctx, t0 + per * kB);
     const int nblk = (t1 - t0 + kB - 1) / kB;
@@ -991,6 +1128,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a
     const int tid = threadIdx.x;
     const int row = blockIdx.x * RPB + tid / LPR;  // s * Hq + h
     const int d0 = (tid % LPR) * 4;
+    const int P = merge_partition_len(a);
     if (row >= a.S * a.Hq) return;
     const int s = row / a.Hq;
     const float *pml = a.part_ml + (int64_t)row * a.NP * 2;
@@ -1005,7 +1143,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeArgs a
         }
     }
     const int ctx = seq_ctx(a, s);
-    const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
+    const int np = ctx > P ? (ctx + P - 1) / P : 1;
     if (np <= 1) return;  // written by the partition kernel
     LseState st;
 #pragma unroll
@@ -1041,8 +1179,9 @@ __global__ __launch_bounds__(kMergeWideThreads) void merge_wide_kernel(const Dec
     const int tid = threadIdx.x;
     const int grp = tid / LPR, lg = tid % LPR, d0 = lg * 4;
     const int s = row / a.Hq;
+    const int P = merge_partition_len(a);
     const int ctx = seq_ctx(a, s);
-    const int np = ctx > a.P ? (ctx + a.P - 1) / a.P : 1;
+    const int np = ctx > P ? (ctx + P - 1) / P : 1;
     if (np <= 1) return;  // the whole workgroup: written by the partition kernel
     const float *pml = a.part_ml + (int64_t)row * a.NP * 2;
     const float *po = a.part_o + (int64_t)row * a.NP * D + d0;

@@ -104,6 +104,31 @@ __device__ __forceinline__ float xor32_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Integer sum / maximum over the 64 lanes of a wave, returned in every lane:
+// DPP butterflies within each row of 16 (quad swaps, then the mirrors of
+// half-rows and rows), then the row swaps above.  Every lane of the wave must
+// be active.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = (int)r[0] + (int)r[1];
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (int)r[0] + (int)r[1];
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((int)r[0], (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+
 // ---- loads -----------------------------------------------------------------
 __device__ __forceinline__ i32x4 ld16(const void *p) { return *(const i32x4 *)p; }
 __device__ __forceinline__ i32x2 ld8(const void *p) { return *(const i32x2 *)p; }

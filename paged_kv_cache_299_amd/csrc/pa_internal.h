@@ -20,6 +20,13 @@ struct DecodeArgs {
     float scale_log2_abs;   // |scale| * log2(e)
     int q_xor;              // 0x80008000 when scale < 0: flips the sign of 16-bit q
     int S, Hq, Hkv, G, MB, NP, P;
+    // plan != 0: the partition length is chosen by every workgroup from the
+    // context lengths (device_plan in pa_decode.hip) among 512, 640, ...,
+    // 1024 tokens; P and NP then describe the shortest, which sizes the grid
+    // and the partials.  cus: compute units of the device, for that choice.
+    int plan;
+    int cus;
+    int *plan_slot;         // plan: workgroup 0 of the partition kernel stores P here for the merge
     int BS;                 // tokens per block: 16, or 8 / 32 (matrix-core kernel only)
     int64_t NB;
     int num_units;          // workgroups of the launch: an upper bound on the units
