@@ -388,7 +388,11 @@ __device__ __forceinline__ void merge_row_in_l2(const DecodeArgs &a, int s, int 
 // needed.  (Keeping the new token in registers and patching the loaded
 // operands instead took 28 more registers and a wave per SIMD: 56.8 us on
 // the Llama-3-8B step against 51.5 for the decode alone.)
-template <int DT, int D, bool SPLIT, int POLICY, int BS = 16, bool APPEND = false>
+//
+// PLAN: the partition length is planned in the kernel (DecodeArgs::plan); a
+// kernel of its own, so that launches with a given length carry no plan code.
+template <int DT, int D, bool SPLIT, int POLICY, int BS = 16, bool APPEND = false,
+          bool PLAN = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_mfma_kernel(const DecodeArgs a) {
     static_assert(DT == kBF16 || DT == kF16, "MFMA path takes 16-bit data");
@@ -403,8 +407,13 @@ void decode_mfma_kernel(const DecodeArgs a) {
     const int n = lane & 15;
     const int j = lane >> 4;
     int P, s, ctx, r;
-    if (!unit_of(blockIdx.x, a, a.Hkv, P, s, ctx, r)) return;
-    if (a.plan && blockIdx.x == 0 && lane == 0) *a.plan_slot = P;  // for the merge kernel
+    if constexpr (PLAN) {
+        if (!plan_find_unit(blockIdx.x, a, a.Hkv, P, s, ctx, r)) return;
+        if (blockIdx.x == 0 && lane == 0) *a.plan_slot = P;  // for the merge kernel
+    } else {
+        P = a.P;
+        if (!find_unit(blockIdx.x, a, P, a.Hkv, s, ctx, r)) return;
+    }
     const int g = r % a.Hkv;
     const int p = r / a.Hkv;
     const int per = blocks_per_partition(ctx, P);
@@ -1217,6 +1226,14 @@ __global__ __launch_bounds__(kMergeWideThreads) void merge_wide_kernel(const Dec
 }
 
 // ---------------------------------------------------------------------------
+template <int DT, int D, int POLICY, bool APPEND, bool PLAN>
+static void launch_mfma16(const DecodeArgs &a, bool split, int grid, hipStream_t stream) {
+    if (split)
+        decode_mfma_kernel<DT, D, true, POLICY, 16, APPEND, PLAN><<<grid, 64, 0, stream>>>(a);
+    else
+        decode_mfma_kernel<DT, D, false, POLICY, 16, APPEND, PLAN><<<grid, 64, 0, stream>>>(a);
+}
+
 template <int DT, int D>
 static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream_t stream) {
     // one workgroup per possible unit (the host plans for full tables); the
@@ -1237,24 +1254,23 @@ static hipError_t launch_typed(const DecodeArgs &a, DecodeKernel kind, hipStream
                     else
                         decode_mfma_kernel<DT, D, false, kCachePolicyNT, 8><<<grid, 64, 0, stream>>>(a);
                 }
-            } else if (kind == DecodeKernel::kMfma && a.k_new) {
-                const bool split = 2 * a.G <= 16;
-                if (split)
-                    decode_mfma_kernel<DT, D, true, kCachePolicyNT, 16, true><<<grid, 64, 0, stream>>>(a);
-                else
-                    decode_mfma_kernel<DT, D, false, kCachePolicyNT, 16, true><<<grid, 64, 0, stream>>>(a);
             } else if (kind == DecodeKernel::kMfma) {
                 const bool split = 2 * a.G <= 16;
-                if (a.shared_blocks) {
-                    if (split)
-                        decode_mfma_kernel<DT, D, true, kCachePolicyPlain><<<grid, 64, 0, stream>>>(a);
+                if (a.k_new) {
+                    if (a.plan)
+                        launch_mfma16<DT, D, kCachePolicyNT, true, true>(a, split, grid, stream);
                     else
-                        decode_mfma_kernel<DT, D, false, kCachePolicyPlain><<<grid, 64, 0, stream>>>(a);
+                        launch_mfma16<DT, D, kCachePolicyNT, true, false>(a, split, grid, stream);
+                } else if (a.shared_blocks) {
+                    if (a.plan)
+                        launch_mfma16<DT, D, kCachePolicyPlain, false, true>(a, split, grid, stream);
+                    else
+                        launch_mfma16<DT, D, kCachePolicyPlain, false, false>(a, split, grid, stream);
                 } else {
-                    if (split)
-                        decode_mfma_kernel<DT, D, true, kCachePolicyNT><<<grid, 64, 0, stream>>>(a);
+                    if (a.plan)
+                        launch_mfma16<DT, D, kCachePolicyNT, false, true>(a, split, grid, stream);
                     else
-                        decode_mfma_kernel<DT, D, false, kCachePolicyNT><<<grid, 64, 0, stream>>>(a);
+                        launch_mfma16<DT, D, kCachePolicyNT, false, false>(a, split, grid, stream);
                 }
             } else {
                 decode_valu_kernel<DT, D><<<dim3(grid), dim3(64), 0, stream>>>(a);
