@@ -888,8 +888,7 @@ def bench_vattention(args, dev):
         "step_map_ms": round(step_ms, 2),
         "create_us_per_page": round(info["create_us_per_page"], 2),
         "map_us_per_page": round(info["map_us_per_page"], 2),
-        "launch": f"HIP graph replays, {G} steps per graph (one decode iteration of a "
-                  f"{G}-layer model), layer pools rotated",
+        "launch": "HIP graph replays, one graph per pass over the rotated layers",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "kernel": "pa_vkv_decode (partition + merge kernels, no block table)",

@@ -394,9 +394,15 @@ typedef struct pa_vkv pa_vkv;
 /* Reserve the virtual ranges.  page_bytes 0 = the device's recommended
  * allocation granularity (hipMemGetAllocationGranularity) doubled up to at
  * least 2 MiB, else a multiple of the minimum granularity.
- * max_context_len a multiple of 16.  Errors: PA_ERR_INVALID_ARG (sizes,
- * dtype, page size), PA_ERR_UNSUPPORTED (no virtual memory management on the
- * device, or pages and 16-token blocks that do not tile a slot), PA_ERR_HIP. */
+ * max_context_len a multiple of 16.  Every page is a physical allocation of
+ * its own, and the runtime holds about 32K of them per process (the
+ * 32,757th hipMemCreate fails on MI355X with ROCm 7.2): a storage whose
+ * pages, mapped in every slot of its 2 * num_layers buffers, would number
+ * more than 24,576 is refused, with the smallest page size that fits in the
+ * message (64 KiB pages fit 1.5 GiB of mapped storage).  Errors:
+ * PA_ERR_INVALID_ARG (sizes, dtype, page size), PA_ERR_UNSUPPORTED (no
+ * virtual memory management on the device, pages and 16-token blocks that
+ * do not tile a slot, or too many pages), PA_ERR_HIP. */
 int pa_vkv_create(int num_layers, int max_batch, int max_context_len, int num_kv_heads,
                   int head_dim, int dtype, int64_t page_bytes, pa_vkv **out);
 
@@ -416,7 +422,8 @@ int pa_vkv_alloc_reqid(pa_vkv *v, int *req_id);
 
 /* Map pages so that slot r holds seq_lens[r] tokens (host int32
  * [max_batch]) in every layer.  Never unmaps.  PA_ERR_NO_MEMORY when the
- * device runs out of memory (pages mapped before the failure stay). */
+ * device runs out of memory, or the process out of page allocations (pages
+ * mapped before the failure stay). */
 int pa_vkv_step(pa_vkv *v, const int32_t *seq_lens);
 
 /* Release a slot; its pages stay mapped until pa_vkv_reclaim. */

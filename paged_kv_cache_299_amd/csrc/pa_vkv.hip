@@ -101,6 +101,9 @@ void teardown(pa_vkv *v) {
 
 }  // namespace
 
+// Page allocations one storage may hold at most (see pa_vkv_create).
+constexpr int64_t kMaxPages = 24576;
+
 int pa_vkv_create(int num_layers, int max_batch, int max_context_len, int num_kv_heads,
                   int head_dim, int dtype, int64_t page_bytes, pa_vkv **out) {
     if (!out) return fail(PA_ERR_INVALID_ARG, "pa_vkv_create: null handle pointer");
@@ -147,6 +150,25 @@ int pa_vkv_create(int num_layers, int max_batch, int max_context_len, int num_kv
     if (req_bytes % block_bytes != 0 || req_bytes / block_bytes > 0x7fffffff / max_batch)
         return fail(PA_ERR_UNSUPPORTED, "pa_vkv_create: pages and 16-token blocks do not tile "
                     "a request's range");
+    // Every page is a physical allocation of its own (hipMemCreate), and the
+    // runtime holds at most ~32K of them per process (on MI355X with ROCm
+    // 7.2 the 32,757th fails, whatever the page size and free memory).  The
+    // storage may map a page in every slot of every buffer, so refuse page
+    // sizes whose worst case passes kMaxPages, and name one that fits.
+    const int64_t worst = 2LL * num_layers * max_batch * (req_bytes / page);
+    if (worst > kMaxPages) {
+        int64_t fit = (int64_t)gran;
+        while (2LL * num_layers * max_batch * ((S + fit - 1) / fit) > kMaxPages) fit *= 2;
+        char msg[320];
+        snprintf(msg, sizeof msg,
+                 "pa_vkv_create: %lld-byte pages need up to %lld page allocations (2 x %d "
+                 "layers x %d slots x %lld pages), past the %lld this library allows per "
+                 "storage (the runtime holds about 32K per process); use pages of at least "
+                 "%lld bytes",
+                 (long long)page, (long long)worst, num_layers, max_batch,
+                 (long long)(req_bytes / page), (long long)kMaxPages, (long long)fit);
+        return fail(PA_ERR_UNSUPPORTED, msg);
+    }
 
     pa_vkv *v = new pa_vkv;
     v->layers = num_layers;
@@ -266,8 +288,12 @@ int pa_vkv_step(pa_vkv *v, const int32_t *seq_lens) {
                         (void)hipMemRelease(handle_at(v, (int)c, r, p));
                     }
                     if (grew) (void)upload_mapped(v);
-                    return fail(PA_ERR_NO_MEMORY, "pa_vkv_step: hipMemCreate failed (out of "
-                                "device memory?)");
+                    char msg[200];
+                    snprintf(msg, sizeof msg,
+                             "pa_vkv_step: hipMemCreate failed after %lld pages (out of device "
+                             "memory, or of the runtime's ~32K allocations per process)",
+                             (long long)v->pages_created);
+                    return fail(PA_ERR_NO_MEMORY, msg);
                 }
                 err = hipMemMap(addr, (size_t)v->page, 0, h, 0);
                 if (err == hipSuccess) err = hipMemSetAccess(addr, (size_t)v->page, &access, 1);

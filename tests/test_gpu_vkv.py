@@ -8,6 +8,7 @@ import torch
 
 import oracle
 import paged_kv_cache_299_amd as pa
+from paged_kv_cache_299_amd import PAError
 from paged_kv_cache_299_amd.layout import kv_cache_shapes
 
 from helpers import CODE, raw
@@ -145,6 +146,39 @@ def test_vkv_growth_deferred_reclamation_and_reuse(dev):
         st = vkv.info()
         log(f"  create {st['create_us_per_page']:.1f} us/page, map {st['map_us_per_page']:.1f} "
             f"us/page")
+    finally:
+        vkv.close()
+
+
+def test_vkv_small_pages(dev):
+    """64 KiB pages: refused where mapping every slot would need more page
+    allocations than the runtime holds per process (the error names a page
+    size that fits), and usable where they fit: growth, decode, reclaim."""
+    with pytest.raises(PAError, match="use pages of at least"):
+        pa.VirtualKV(num_layers=8, max_batch=32, max_context_len=4096, num_kv_heads=8,
+                     head_dim=128, dtype=torch.bfloat16, page_bytes=64 << 10)
+    vkv = pa.VirtualKV(num_layers=1, max_batch=4, max_context_len=4096, num_kv_heads=8,
+                       head_dim=128, dtype=torch.bfloat16, page_bytes=64 << 10)
+    try:
+        assert vkv.page_bytes == 64 << 10
+        block = B * 8 * 128 * 2            # 32 KiB: two blocks per page
+        a, b = vkv.alloc_reqid(), vkv.alloc_reqid()
+        lens = [0] * 4
+        lens[a], lens[b] = 33, 1000
+        vkv.step(lens)
+        pages = lambda n: -(-(-(-n // B) * block) // (64 << 10))   # noqa: E731
+        assert vkv.info()["mapped_bytes"] == 2 * (64 << 10) * (pages(33) + pages(1000))
+        m = Mirror(vkv, dev, seed=7)
+        m.write(0, _tokens(a, 0, 33) + _tokens(b, 0, 1000))
+        m.check(0, [a, b], [33, 1000], 32, "64 KiB pages")
+        lens[a] = 4096
+        vkv.step(lens)
+        m.write(0, _tokens(a, 33, 4096))
+        m.check(0, [b, a], [1000, 4096], 32, "64 KiB pages, grown")
+        vkv.free_reqid(b)
+        vkv.reclaim()
+        assert vkv.info()["mapped_bytes"] == 2 * (64 << 10) * pages(4096)
+        m.check(0, [a], [4096], 8, "64 KiB pages, after reclaim")
     finally:
         vkv.close()
 
