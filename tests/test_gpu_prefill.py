@@ -191,3 +191,26 @@ def test_workload_full_size_sampled_rows(dev, name):
     # +-2, where the bf16 output's own rounding alone exceeds 2e-3, so the
     # bound is 2e-3 beyond that rounding, as for every other prefill case
     check_decode(out[rows], ref, case.dtype, f"{name} ({len(rows)} sampled rows)")
+
+
+@pytest.mark.parametrize("name", ["prefill_llama3_8b", "prefill_chunked_llama3_8b"])
+def test_workload_full_size_every_row_of_one_sequence(dev, name):
+    """Every row of one full-size sequence of the benchmark workloads (the one
+    with the fewest keys to score: a 2,078-token prompt; a 1,024-token chunk
+    over a 3,459-token prefix), in the benchmark's launch configuration,
+    against the oracle's prefill of that sequence alone."""
+    case = workloads.CASES[name]()
+    g = GpuPrefill(case, dev)
+    out = g.run(max_query_len=case.max_query_len)
+    ctx = case.context_lens.tolist()
+    n = list(case.query_lens)
+    s = min(range(len(ctx)), key=lambda i: n[i] * (ctx[i] - n[i]) + n[i] * (n[i] + 1) // 2)
+    log(f"prefill full size {name}: sequence {s}, {n[s]} queries over {ctx[s]} tokens")
+    kc, vc = _oracle_pools(case)
+    qs = case.query_start.tolist()
+    rows = slice(qs[s], qs[s + 1])
+    ref = oracle.prefill(raw(case.q[rows]), kc, vc, case.block_tables.numpy()[s:s + 1],
+                         np.array([ctx[s]], np.int32), np.array([0, n[s]], np.int32), case.scale,
+                         num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                         block_size=case.block_size, k_x=_x(case.dtype), dtype=CODE[case.dtype])
+    check_decode(out[rows], ref, case.dtype, f"{name} sequence {s}, all {n[s]} rows")
