@@ -23,6 +23,19 @@ namespace pa {
 // write one contiguous 16-slot row segment, which L2 merges into whole lines
 // (storing aligned 8-token runs as 16-byte pieces instead measured no faster
 // on a 290 MB bulk write and slower on one-token appends).
+// A slot splits into (block, offset) once per token: a power-of-two block size
+// (every layout the decode reads) takes a shift and a mask, any other size
+// one 64-bit division.
+__device__ inline void split_slot(int64_t slot, int B, int log2B, int64_t &blk, int &off) {
+    if (log2B >= 0) {
+        blk = slot >> log2B;
+        off = (int)(slot & (B - 1));
+    } else {
+        blk = slot / B;
+        off = (int)(slot - blk * B);
+    }
+}
+
 template <int E>
 __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ k_new,
                                                        const char *__restrict__ v_new,
@@ -30,13 +43,15 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
                                                        char *__restrict__ v_cache,
                                                        const int64_t *__restrict__ slots,
                                                        int64_t num_tokens, int Hkv, int D, int B,
-                                                       int64_t num_slots,
+                                                       int log2B, int64_t num_slots,
                                                        const int *__restrict__ mapped,
                                                        int req_stride, int num_req) {
     constexpr int X = 16 / E;
     // TT rows of D*E/4 words plus one pad word each: TT * D*E/4 <= 1024 and TT <= 256
     __shared__ uint32_t vtile[1024 + 256];
-    __shared__ int64_t slot_sh[256];
+    // per token: element offset of its (block, kv head) tile plus its offset in
+    // the block, or -1 for a token that is skipped
+    __shared__ int64_t base_sh[256];
     const int NC = D / X;        // 16-byte runs per head vector (1..128)
     const int TT = 256 / NC;     // tokens per tile
     const int tid = threadIdx.x;
@@ -62,16 +77,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
         const int64_t per_req = (int64_t)req_stride * B;
         const int64_t r = slot / per_req;
         ok = r < num_req && slot - r * per_req < mapped[r];
-        if (!ok) slot = -1;
     }
-    if (ok) {
-        const int64_t blk = slot / B;
-        const int off = (int)(slot % B);
-        const int64_t tile = (blk * Hkv + g) * (int64_t)D * B;  // elements
-        *(i32x4 *)(k_cache + (tile + ((int64_t)c * B + off) * X) * E) = kv;
-    }
+    int64_t blk = 0;
+    int off = 0;
+    if (ok) split_slot(slot, B, log2B, blk, off);
+    const int64_t tile = (blk * Hkv + g) * (int64_t)D * B;  // elements
+    if (ok) *(i32x4 *)(k_cache + (tile + ((int64_t)c * B + off) * X) * E) = kv;
     if (tt < TT) {
-        if (c == 0) slot_sh[tt] = slot;
+        if (c == 0) base_sh[tt] = ok ? tile + off : -1;
         uint32_t *row = vtile + tt * row_words + c * 4;
         row[0] = (uint32_t)vv[0];
         row[1] = (uint32_t)vv[1];
@@ -85,11 +98,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
     for (int e = tid; e < TT * D; e += 256) {
         const int et = e % TT, d = e / TT;
         if (et >= ntok) continue;
-        const int64_t sl = slot_sh[et];
-        if (sl < 0 || sl >= num_slots) continue;
-        const int64_t blk = sl / B;
-        const int off = (int)(sl % B);
-        char *dst = v_cache + (((blk * Hkv + g) * D + d) * (int64_t)B + off) * E;
+        const int64_t base = base_sh[et];
+        if (base < 0) continue;
+        char *dst = v_cache + (base + (int64_t)d * B) * E;
         const char *src = (const char *)(vtile + et * row_words) + d * E;
         if constexpr (E == 4) {
             *(uint32_t *)dst = *(const uint32_t *)src;
@@ -140,14 +151,15 @@ hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, 
     const int64_t tiles = (T + TT - 1) / TT;
     if (tiles * Hkv > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tiles * Hkv));
+    const int log2B = (B & (B - 1)) == 0 ? __builtin_ctz((unsigned)B) : -1;
     if (elem_bytes == 4) {
         write_kv_kernel<4><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
-            Hkv, D, B, NB * B, mapped, req_stride, num_req);
+            Hkv, D, B, log2B, NB * B, mapped, req_stride, num_req);
     } else {
         write_kv_kernel<2><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,
-            Hkv, D, B, NB * B, mapped, req_stride, num_req);
+            Hkv, D, B, log2B, NB * B, mapped, req_stride, num_req);
     }
     return hipGetLastError();
 }
