@@ -110,6 +110,59 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char *__restrict__ 
     }
 }
 
+// Few tokens (a decode step): one wave takes 64 / NC tokens of one kv head,
+// lane -> (token, 16-byte run), and stores its run's x V elements itself, x
+// two-byte stores at a stride of one B-slot row, with no LDS round trip and
+// no barrier.  The tokens of a decode step go to scattered slots, so the
+// V stores could not merge in L2 anyway; more, smaller workgroups spread the
+// stores over more compute units.
+template <int E>
+__global__ __launch_bounds__(64) void write_kv_few_kernel(const char *__restrict__ k_new,
+                                                          const char *__restrict__ v_new,
+                                                          char *__restrict__ k_cache,
+                                                          char *__restrict__ v_cache,
+                                                          const int64_t *__restrict__ slots,
+                                                          int64_t num_tokens, int Hkv, int D,
+                                                          int B, int log2B, int64_t num_slots,
+                                                          const int *__restrict__ mapped,
+                                                          int req_stride, int num_req) {
+    constexpr int X = 16 / E;
+    const int NC = D / X;      // 16-byte runs per head vector (1..64)
+    const int TW = 64 / NC;    // tokens per wave
+    const int lane = threadIdx.x;
+    const int g = (int)(blockIdx.x % (unsigned)Hkv);
+    const int tt = lane / NC, c = lane % NC;
+    const int64_t t = (int64_t)(blockIdx.x / (unsigned)Hkv) * TW + tt;
+    if (tt >= TW || t >= num_tokens) return;
+    const int64_t src = ((t * Hkv + g) * D) * E + (int64_t)c * 16;
+    const int64_t slot = slots[t];
+    const i32x4 kv = ld16(k_new + src);
+    const i32x4 vv = ld16(v_new + src);
+    bool ok = slot >= 0 && slot < num_slots;
+    if (ok && mapped) {
+        const int64_t per_req = (int64_t)req_stride * B;
+        const int64_t r = slot / per_req;
+        ok = r < num_req && slot - r * per_req < mapped[r];
+    }
+    if (!ok) return;
+    int64_t blk;
+    int off;
+    split_slot(slot, B, log2B, blk, off);
+    const int64_t tile = (blk * Hkv + g) * (int64_t)D * B;  // elements
+    *(i32x4 *)(k_cache + (tile + ((int64_t)c * B + off) * X) * E) = kv;
+    char *vd = v_cache + (tile + (int64_t)c * X * B + off) * E;
+    if constexpr (E == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *(uint32_t *)(vd + (int64_t)e * B * 4) = (uint32_t)vv[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = (uint32_t)vv[e >> 1];
+            *(uint16_t *)(vd + (int64_t)e * B * 2) = (uint16_t)((e & 1) ? (w >> 16) : w);
+        }
+    }
+}
+
 // grid.y walks the pairs, grid.x the 16-byte runs of one block of one pool.
 // Block src of the source pools goes to block dst of the destination pools.
 // The pools may be the same allocations (copy-on-write: no destination is a
@@ -141,6 +194,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const char *__restrict
     }
 }
 
+// Up to this many tokens (a decode step's batch) take the one-wave kernel.
+constexpr int64_t kFewTokens = 1024;
+
 hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                            const int64_t *slots, int64_t T, int Hkv, int D, int B, int64_t NB,
                            int elem_bytes, hipStream_t stream, const int *mapped, int req_stride,
@@ -152,6 +208,20 @@ hipError_t launch_write_kv(const void *k_new, const void *v_new, void *k_cache, 
     if (tiles * Hkv > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(tiles * Hkv));
     const int log2B = (B & (B - 1)) == 0 ? __builtin_ctz((unsigned)B) : -1;
+    if (T <= kFewTokens && NC <= 64) {
+        const int TW = 64 / NC;
+        const dim3 fgrid((unsigned)(((T + TW - 1) / TW) * Hkv));
+        if (elem_bytes == 4) {
+            write_kv_few_kernel<4><<<fgrid, dim3(64), 0, stream>>>(
+                (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots,
+                T, Hkv, D, B, log2B, NB * B, mapped, req_stride, num_req);
+        } else {
+            write_kv_few_kernel<2><<<fgrid, dim3(64), 0, stream>>>(
+                (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots,
+                T, Hkv, D, B, log2B, NB * B, mapped, req_stride, num_req);
+        }
+        return hipGetLastError();
+    }
     if (elem_bytes == 4) {
         write_kv_kernel<4><<<grid, dim3(256), 0, stream>>>(
             (const char *)k_new, (const char *)v_new, (char *)k_cache, (char *)v_cache, slots, T,

@@ -186,6 +186,41 @@ def test_write_kv_runs_of_consecutive_slots(dev, dtype):
     assert same_bits(g.k.cpu(), kc) and same_bits(g.v.cpu(), vc)
 
 
+@pytest.mark.parametrize("T", [1, 1024, 1025, 3000])
+@pytest.mark.parametrize("dtype,D,B", [(torch.bfloat16, 128, 16), (torch.float16, 64, 7),
+                                       (torch.float32, 32, 32), (torch.bfloat16, 24, 5)])
+def test_write_kv_both_kernels(dev, T, dtype, D, B):
+    """Up to 1,024 tokens take the one-wave kernel, more the LDS-transposing
+    one; block sizes that are not powers of two take the division path.
+    Half of the tokens go to consecutive slots, the rest scattered, some skipped."""
+    log(f"write_kv T={T} {dtype} D={D} B={B}")
+    from helpers import CODE, raw
+    import oracle
+    Hkv = 3
+    NB = (2 * T) // B + 8
+    rng = np.random.default_rng(T * 31 + D + B)
+    free = rng.permutation(NB * B)
+    n_run = T // 2
+    start = int(rng.integers(0, NB * B - n_run)) if n_run else 0
+    run = np.arange(start, start + n_run)
+    rest = np.setdiff1d(free, run, assume_unique=False)
+    rest = rng.permutation(rest)[: T - n_run]
+    slots = np.concatenate([run, rest]).astype(np.int64)
+    slots[rng.random(T) < 0.1] = -1
+    ks, vs = pa.kv_cache_shapes(NB, Hkv, D, B, dtype)
+    kc = torch.from_numpy(rng.standard_normal(ks).astype(np.float32)).to(dtype)
+    vc = torch.from_numpy(rng.standard_normal(vs).astype(np.float32)).to(dtype)
+    kn = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(dtype)
+    vn = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(dtype)
+    kg, vg = kc.to(dev), vc.to(dev)
+    pa.pa_write_kv(kn.to(dev), vn.to(dev), kg, vg, torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    x = 16 // torch.tensor([], dtype=dtype).element_size()
+    ko, vo = oracle.write_kv(raw(kn), raw(vn), raw(kc), raw(vc), slots, num_kv_heads=Hkv,
+                             head_dim=D, block_size=B, k_x=x, dtype=CODE[dtype])
+    assert same_bits(kg.cpu(), ko) and same_bits(vg.cpu(), vo)
+
+
 def test_copy_blocks_bit_exact(dev):
     log("copy_blocks")
     case = _case([40, 3, 160], 32, 32, 128, torch.bfloat16, seed=8, NB=200)
