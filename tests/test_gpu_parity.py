@@ -527,3 +527,46 @@ def test_force_valu_full_size(dev, name):
     kc, vc = oracle_apply_steps(case)
     check_decode(_force_valu_run(case, dev, 0), oracle_decode(case, kc, vc), case.dtype,
                  f"force_valu {name}", strict=True)
+
+
+# --------------------------------------------------------------------------
+# a seeded sweep over shapes, lengths, partition lengths and launch flags
+# --------------------------------------------------------------------------
+_SWEEP_HEADS = [(1, 1), (4, 4), (8, 2), (32, 8), (16, 1), (40, 40), (12, 4), (64, 4), (24, 8)]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_sweep(dev, seed):
+    """Per seed: a head layout (G = 1 .. 16 on the matrix cores, 16 and more
+    on the vector kernel with fp32), a dtype, a head size, 1-40 sequences
+    whose lengths mix the edges (0, 1, 15, 16, 17, partition boundaries) with
+    uniform draws up to 3,000 tokens, and a launch: the plain entry point,
+    an explicit partition length, the forced merge kernel, the shared-blocks
+    hint or the vector kernel.  Pools are scattered over spare blocks."""
+    rng = np.random.default_rng(1000 + seed)
+    Hq, Hkv = _SWEEP_HEADS[seed % len(_SWEEP_HEADS)]
+    dtype = [torch.bfloat16, torch.float16, torch.float32][int(rng.integers(0, 3))]
+    D = [64, 128][int(rng.integers(0, 2))]
+    S = int(rng.integers(1, 41))
+    edges = [0, 1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025]
+    ctxs = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(1, 3001))
+            for _ in range(S)]
+    if max(ctxs) == 0:
+        ctxs[0] = 1
+    launch = ["plain", "P", "merge_kernel", "shared", "valu"][int(rng.integers(0, 5))]
+    P = 16 * int(rng.integers(1, 65)) if launch in ("P", "merge_kernel", "shared", "valu") else 0
+    if launch == "valu" and dtype == torch.float32:
+        launch = "P"  # fp32 takes the vector kernel already
+    spare = int(rng.integers(0, 200))
+    case = _case(ctxs, Hq, Hkv, D, dtype, seed=2000 + seed, NB=sum(-(-c // 16) for c in ctxs) + 7 + spare)
+    log(f"sweep {seed}: Hq={Hq} Hkv={Hkv} D={D} {dtype} S={S} launch={launch} P={P} "
+        f"max ctx {max(ctxs)}")
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    kw = dict(partition_tokens=P, merge_kernel=launch == "merge_kernel",
+              shared_blocks=launch == "shared", force_valu=launch == "valu")
+    pa.pa_decode(g.q, g.k, g.v, g.bt, g.cl, case.scale, g.out, **kw)
+    torch.cuda.synchronize()
+    kc, vc = oracle_apply_steps(case)
+    ref = oracle_decode(case, kc, vc)
+    check_decode(g.out.cpu(), ref, dtype, f"sweep {seed}")
