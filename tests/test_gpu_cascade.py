@@ -128,3 +128,23 @@ def test_workload_full_size(dev, name):
     sequences, 16 groups), in the benchmark's launch configuration."""
     case = workloads.CASES[name]()
     _check(case, dev, name, strict=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_sweep(dev, seed):
+    """Per seed: parallel sampling with a random number of prompts (1-6),
+    samples per prompt (1-8), prompt length (block-aligned or not, with or
+    without copy-on-write), private tokens, head layout and partition
+    length; groups found from the tables."""
+    rng = np.random.default_rng(5000 + seed)
+    Hq, Hkv = [(8, 8), (16, 4), (32, 8), (8, 1), (12, 4), (4, 4)][seed % 6]
+    cow = bool(rng.integers(0, 2))
+    prompt = 16 * int(rng.integers(1, 40)) - (8 if cow else 0)
+    case = workloads.parallel_sampling(seed=6000 + seed, cow=cow,
+                                       num_prompts=int(rng.integers(1, 7)),
+                                       samples=int(rng.integers(1, 9)), prompt_tokens=prompt,
+                                       max_private=int(rng.integers(1, 300)), num_heads=Hq,
+                                       num_kv_heads=Hkv, num_blocks=1024)
+    P = [0, 16 * int(rng.integers(1, 65))][int(rng.integers(0, 2))]
+    _check(case, dev, f"sweep {seed}: Hq={Hq} Hkv={Hkv} cow={cow} prompt={prompt} P={P}",
+           partition_tokens=P)

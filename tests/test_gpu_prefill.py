@@ -214,3 +214,30 @@ def test_workload_full_size_every_row_of_one_sequence(dev, name):
                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
                          block_size=case.block_size, k_x=_x(case.dtype), dtype=CODE[case.dtype])
     check_decode(out[rows], ref, case.dtype, f"{name} sequence {s}, all {n[s]} rows")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_sweep(dev, seed):
+    """Per seed: a head layout, bf16 or fp16, head size 64 or 128, 1-12
+    sequences whose chunks mix whole prompts, chunks after a cached prefix,
+    single queries and empty chunks, lengths up to 1,200 tokens with block
+    and row-tile edges, and spare pool blocks."""
+    rng = np.random.default_rng(3000 + seed)
+    Hq, Hkv = [(4, 4), (8, 2), (32, 8), (16, 1), (12, 4), (40, 40)][seed % 6]
+    dtype = [torch.bfloat16, torch.float16][int(rng.integers(0, 2))]
+    D = [64, 128][int(rng.integers(0, 2))]
+    S = int(rng.integers(1, 13))
+    edges = [1, 15, 16, 17, 31, 32, 33, 127, 128, 129]
+    ctxs, qlens = [], []
+    for _ in range(S):
+        c = int(rng.choice(edges)) if rng.random() < 0.3 else int(rng.integers(1, 1201))
+        kind = int(rng.integers(0, 4))
+        n = c if kind == 0 else (1 if kind == 1 else (0 if kind == 2 else int(rng.integers(1, c + 1))))
+        ctxs.append(c)
+        qlens.append(n)
+    if sum(qlens) == 0:
+        qlens[0] = ctxs[0]
+    NB = sum(-(-c // 16) for c in ctxs) + 5 + int(rng.integers(0, 100))
+    case = _case(ctxs, qlens, Hq, Hkv, D, dtype, seed=4000 + seed, NB=NB)
+    _check(case, dev, f"sweep {seed}: Hq={Hq} Hkv={Hkv} D={D} {dtype} S={S} "
+                      f"queries {sum(qlens)}")
