@@ -222,7 +222,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels are "
-              "single-device and this build measures one GPU's share.", file=sys.stderr)
+              "single-device and the benchmark measures one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

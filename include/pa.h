@@ -54,7 +54,7 @@ extern "C" {
 typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1, /* a size, pointer or dtype the call cannot accept */
-    PA_ERR_UNSUPPORTED = 2, /* valid, but not a shape this build implements */
+    PA_ERR_UNSUPPORTED = 2, /* valid, but not a shape the library implements */
     PA_ERR_HIP = 3,         /* the HIP runtime reported an error */
     PA_ERR_NO_MEMORY = 4    /* the library could not allocate its workspace */
 } pa_status;
