@@ -570,3 +570,59 @@ def test_random_sweep(dev, seed):
     kc, vc = oracle_apply_steps(case)
     ref = oracle_decode(case, kc, vc)
     check_decode(g.out.cpu(), ref, dtype, f"sweep {seed}")
+
+
+# --------------------------------------------------------------------------
+# pools past 4 GiB: 64-bit tile and slot offsets
+# --------------------------------------------------------------------------
+def test_pools_past_4_gib(dev):
+    """A 160,000-block pool (5.2 GB for K, 5.2 GB for V at 8 kv heads, D 128,
+    bf16): a batch's blocks are placed among the highest block ids, so every
+    tile offset and slot passes 2^32 bytes.  The write of the new tokens, the
+    decode (automatic and explicit partitions) and a block copy between high
+    ids must give what the same batch gives on a compact pool: the oracle's
+    decode, and bit-identical blocks."""
+    case = _case([700, 1, 3000, 129, 2048, 16, 517], 32, 8, 128, torch.bfloat16, seed=77)
+    nb_small = case.num_blocks
+    NB = 160_000
+    ks, vs = pa.kv_cache_shapes(NB, 8, 128, 16, torch.bfloat16)
+    assert 8 * 128 * 16 * 2 * NB > (1 << 32)
+    rng = np.random.default_rng(5)
+    big_ids = NB - 1 - rng.permutation(4 * nb_small)[:nb_small]  # small id -> big id
+    big_ids_t = torch.from_numpy(big_ids.astype(np.int64))
+    log(f"pools of {NB} blocks ({2 * 8 * 128 * 16 * 2 * NB / 1e9:.1f} GB); "
+        f"ids {big_ids.min()}..{big_ids.max()}")
+    k_big = torch.empty(ks, dtype=torch.bfloat16, device=dev)
+    v_big = torch.empty(vs, dtype=torch.bfloat16, device=dev)
+    k_big[big_ids_t.to(dev)] = case.k_cache.to(dev)
+    v_big[big_ids_t.to(dev)] = case.v_cache.to(dev)
+    bt = case.block_tables.clone()
+    bt_big = torch.where(bt >= 0, torch.from_numpy(big_ids.astype(np.int32))[bt.clamp(min=0).long()],
+                         bt).to(dev)
+    st = case.steps[0]
+    sl = st.slot_mapping
+    sl_big = torch.where(sl >= 0, big_ids_t[(sl // 16).clamp(min=0)] * 16 + sl % 16, sl).to(dev)
+    pa.pa_write_kv(st.k_new.to(dev), st.v_new.to(dev), k_big, v_big, sl_big)
+    kc, vc = oracle_apply_steps(case)
+    # the written blocks, read back to the compact numbering
+    assert same_bits(k_big[big_ids_t.to(dev)].cpu(), kc)
+    assert same_bits(v_big[big_ids_t.to(dev)].cpu(), vc)
+    ref = oracle_decode(case, kc, vc)
+    q = case.q.to(dev)
+    cl = case.context_lens.to(dev)
+    out = torch.empty_like(q)
+    for P in (0, 256, 1024):
+        pa.pa_decode(q, k_big, v_big, bt_big, cl, case.scale, out, partition_tokens=P)
+        torch.cuda.synchronize()
+        check_decode(out.cpu(), ref, torch.bfloat16, f"pool past 4 GiB, P={P}")
+    # copy-on-write copies between high ids
+    src = big_ids[:5]
+    dst = NB - 1 - np.setdiff1d(np.arange(8 * nb_small), NB - 1 - big_ids)[:5]
+    pairs = torch.from_numpy(np.stack([src, dst], axis=1).astype(np.int64)).to(dev)
+    pa.pa_copy_blocks(k_big, v_big, pairs)
+    torch.cuda.synchronize()
+    s_t, d_t = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    assert torch.equal(k_big[d_t].view(torch.int16), k_big[s_t].view(torch.int16))
+    assert torch.equal(v_big[d_t].view(torch.int16), v_big[s_t].view(torch.int16))
+    del k_big, v_big
+    torch.cuda.empty_cache()

@@ -241,3 +241,35 @@ def test_random_sweep(dev, seed):
     case = _case(ctxs, qlens, Hq, Hkv, D, dtype, seed=4000 + seed, NB=NB)
     _check(case, dev, f"sweep {seed}: Hq={Hq} Hkv={Hkv} D={D} {dtype} S={S} "
                       f"queries {sum(qlens)}")
+
+
+def test_pool_past_4_gib(dev):
+    """The same prompts on a 160,000-block pool (5.2 GB per pool), their
+    blocks among the highest ids: tile offsets and slots past 2^32 bytes."""
+    case = _case([700, 129, 1500], [700, 100, 64], 32, 8, 128, torch.bfloat16, seed=78)
+    nb_small = case.num_blocks
+    NB = 160_000
+    ks, vs = pa.kv_cache_shapes(NB, 8, 128, 16, torch.bfloat16)
+    rng = np.random.default_rng(6)
+    big_ids = NB - 1 - rng.permutation(4 * nb_small)[:nb_small]
+    ids_t = torch.from_numpy(big_ids.astype(np.int64))
+    k_big = torch.empty(ks, dtype=torch.bfloat16, device=dev)
+    v_big = torch.empty(vs, dtype=torch.bfloat16, device=dev)
+    k_big[ids_t.to(dev)] = case.k_cache.to(dev)
+    v_big[ids_t.to(dev)] = case.v_cache.to(dev)
+    bt = case.block_tables
+    bt_big = torch.where(bt >= 0, torch.from_numpy(big_ids.astype(np.int32))[bt.clamp(min=0).long()],
+                         bt).to(dev)
+    st = case.write_step
+    sl = st.slot_mapping
+    sl_big = torch.where(sl >= 0, ids_t[(sl // 16).clamp(min=0)] * 16 + sl % 16, sl).to(dev)
+    pa.pa_write_kv(st.k_new.to(dev), st.v_new.to(dev), k_big, v_big, sl_big)
+    out = torch.full_like(case.q, float("nan")).to(dev)
+    pa.pa_prefill(case.q.to(dev), k_big, v_big, bt_big, case.context_lens.to(dev),
+                  case.query_start.to(dev), case.scale, out)
+    torch.cuda.synchronize()
+    kc, vc = _oracle_pools(case)
+    assert same_bits(k_big[ids_t.to(dev)].cpu(), kc) and same_bits(v_big[ids_t.to(dev)].cpu(), vc)
+    check_decode(out.cpu(), _oracle_prefill(case, kc, vc), torch.bfloat16, "prefill, pool past 4 GiB")
+    del k_big, v_big
+    torch.cuda.empty_cache()
