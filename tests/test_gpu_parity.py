@@ -626,3 +626,18 @@ def test_pools_past_4_gib(dev):
     assert torch.equal(v_big[d_t].view(torch.int16), v_big[s_t].view(torch.int16))
     del k_big, v_big
     torch.cuda.empty_cache()
+
+
+def test_million_token_context(dev):
+    """One sequence of 2^20 tokens (65,536 blocks, the longest table the
+    device plan takes) beside a 3-token one, 4 query heads on one kv head:
+    up to 2,048 partitions per row at P = 512 (the wide merge kernel), the
+    automatic length and P = 1024."""
+    case = _case([1 << 20, 3], 4, 1, 128, torch.bfloat16, seed=79)
+    g = GpuCase(case, dev)
+    g.apply_steps()
+    kc, vc = oracle_apply_steps(case)
+    ref = oracle_decode(case, kc, vc)
+    for P in (0, 512, 1024):
+        out = g.decode(P)
+        check_decode(out, ref, torch.bfloat16, f"2^20 tokens, P={P}")
